@@ -1,0 +1,181 @@
+"""CPU oracle for the indexer path: paged MQA logits and per-row top-k.
+
+TEST INFRASTRUCTURE ONLY. The library's product path never imports this
+package; only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark do. The arithmetic lives in ``oracle.c`` (plain loops, double
+precision, its own FP8/E2M1/E8M0 decoders); this module only builds it with
+gcc and marshals numpy arrays into it.
+
+Definitions followed are stated in the header of ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FP8 = 1
+MXFP4 = 2
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP over rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int, ctypes.c_int64
+        lib.orc_dec_fp8_e4m3.restype = ctypes.c_double
+        lib.orc_dec_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        lib.orc_dec_e2m1.restype = ctypes.c_double
+        lib.orc_dec_e2m1.argtypes = [ctypes.c_uint8]
+        lib.orc_dec_e8m0.restype = ctypes.c_double
+        lib.orc_dec_e8m0.argtypes = [ctypes.c_uint8]
+        lib.orc_decode_logits.restype = i32
+        lib.orc_decode_logits.argtypes = [
+            i32, P, P, P, i32, i32, P, i64, i64, P, i64, i64, i32, i64,
+            P, i64, P, i32, i32, P, i64, i64, P, P]
+        lib.orc_prefill_logits.restype = i32
+        lib.orc_prefill_logits.argtypes = [
+            i32, P, P, P, i32, i32, P, i64, i64, P, i64, i64, i32, i64,
+            P, P, i64, P, i64, i64, P, P]
+        lib.orc_topk_f64.restype = i32
+        lib.orc_topk_f64.argtypes = [P, i64, i32, P]
+        lib.orc_topk_f32.restype = i32
+        lib.orc_topk_f32.argtypes = [P, i64, i32, P]
+        lib.orc_topk_rows_f32.restype = i32
+        lib.orc_topk_rows_f32.argtypes = [P, i64, P, i64, i32, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u8(a):
+    return None if a is None else np.ascontiguousarray(a).view(np.uint8)
+
+
+def dec_fp8(code: int) -> float:
+    return _load().orc_dec_fp8_e4m3(code)
+
+
+def dec_e2m1(nibble: int) -> float:
+    return _load().orc_dec_e2m1(nibble)
+
+
+def dec_e8m0(code: int) -> float:
+    return _load().orc_dec_e8m0(code)
+
+
+class Cache:
+    """Host view of a paged K cache: byte pool + strides (all in bytes)."""
+
+    def __init__(self, dtype, data, page_stride, row_stride, scale,
+                 scale_page_stride, scale_row_stride, page_size, num_pages):
+        self.dtype = dtype
+        self.data = _u8(data)
+        self.page_stride = int(page_stride)
+        self.row_stride = int(row_stride)
+        self.scale = _u8(scale)
+        self.scale_page_stride = int(scale_page_stride)
+        self.scale_row_stride = int(scale_row_stride)
+        self.page_size = int(page_size)
+        self.num_pages = int(num_pages)
+
+
+def decode_logits(dtype, q, q_scale, w, H, D, cache: Cache, block_tables, lens,
+                  next_n, rows, W):
+    """Double-precision logits of the listed decode rows.
+
+    Returns (logits [len(rows), W] float64 with -inf past each row's visible
+    length, E [len(rows)] int64)."""
+    lib = _load()
+    q = _u8(q)
+    qs = _u8(q_scale)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), W), dtype=np.float64)
+    E = np.empty(len(rows), dtype=np.int64)
+    rc = lib.orc_decode_logits(
+        dtype, _ptr(q), _ptr(qs), _ptr(w), H, D, _ptr(cache.data),
+        cache.page_stride, cache.row_stride, _ptr(cache.scale),
+        cache.scale_page_stride, cache.scale_row_stride, cache.page_size,
+        cache.num_pages, _ptr(bt), bt.shape[1], _ptr(lens), len(lens), next_n,
+        _ptr(rows), len(rows), W, _ptr(out), _ptr(E))
+    if rc != 0:
+        raise ValueError("oracle decode_logits failed with code %d" % rc)
+    return out, E
+
+
+def prefill_logits(dtype, q, q_scale, w, H, D, cache: Cache, block_table,
+                   visible_end, rows, W):
+    """Double-precision logits of the listed prefill rows (one sequence)."""
+    lib = _load()
+    q = _u8(q)
+    qs = _u8(q_scale)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32).reshape(-1)
+    ve = np.ascontiguousarray(visible_end, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), W), dtype=np.float64)
+    E = np.empty(len(rows), dtype=np.int64)
+    rc = lib.orc_prefill_logits(
+        dtype, _ptr(q), _ptr(qs), _ptr(w), H, D, _ptr(cache.data),
+        cache.page_stride, cache.row_stride, _ptr(cache.scale),
+        cache.scale_page_stride, cache.scale_row_stride, cache.page_size,
+        cache.num_pages, _ptr(bt), _ptr(ve), len(ve), _ptr(rows), len(rows), W,
+        _ptr(out), _ptr(E))
+    if rc != 0:
+        raise ValueError("oracle prefill_logits failed with code %d" % rc)
+    return out, E
+
+
+def topk(values, E, k):
+    """Top-k token indices of one row (largest first, ties to lower index),
+    padded with -1. float32 input is ordered as float32, float64 as float64."""
+    lib = _load()
+    out = np.empty(k, dtype=np.int32)
+    if values.dtype == np.float32:
+        v = np.ascontiguousarray(values)
+        rc = lib.orc_topk_f32(_ptr(v), int(E), k, _ptr(out))
+    else:
+        v = np.ascontiguousarray(values, dtype=np.float64)
+        rc = lib.orc_topk_f64(_ptr(v), int(E), k, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle topk failed with code %d" % rc)
+    return out
+
+
+def topk_rows_f32(logits, E, k):
+    """Top-k of many float32 rows (row stride = logits.shape[1])."""
+    lib = _load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    E = np.ascontiguousarray(E, dtype=np.int64)
+    out = np.empty((lg.shape[0], k), dtype=np.int32)
+    rc = lib.orc_topk_rows_f32(_ptr(lg), lg.shape[1], _ptr(E), lg.shape[0], k, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle topk_rows failed with code %d" % rc)
+    return out

@@ -1,0 +1,394 @@
+/*
+ * Oracle for the sparse-attention indexer: paged MQA logits and per-row top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path links, loads or calls
+ * this file; only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do. It shares no code, header, table or constant with the HIP
+ * library: its decoders, page translation and selection are written here from
+ * the definitions alone, in plain loops, accumulating in double precision.
+ *
+ * What it computes (sources are the four pull-request pages the method is
+ * described on):
+ *   - The indexer score ("mqa-logits") of one query row against one K token:
+ *       logit = sum_h w[h] * max(0, k_scale * (q_h . k))
+ *     over a single-head K cache. The pages name the op (ROCm/ATOM PR #1709
+ *     "Add fp4 indexer fo dsv4", commit messages on the FP4 mqa-logits kernel
+ *     and on indexer_score_topk; vllm-project/DeepGEMM PR #14, summary, "FP8
+ *     paged-MQA logits") but do not print the formula; the formula above is
+ *     the stated problem this library is built for.
+ *   - The page walk: logical token t of a sequence lives in physical page
+ *     block_table[t / page_size] at slot t % page_size, i.e. cache row
+ *     phys * page_size + slot (ATOM PR #1709, commit on the HCA k2-aware
+ *     offsets, which names this "//capacity, %capacity, phys*capacity+slot"
+ *     pattern as the correct one).
+ *   - The per-row top-k: the min(k, E) largest logits of a row, ties to the
+ *     lower token index, padded with -1 (ATOM PR #1709, commit on routing
+ *     indexer_score_topk; "seq-local" output of the FP4 prefill path).
+ *
+ * Storage formats decoded here (closed forms from the format definitions):
+ *   - OCP FP8 E4M3FN byte: sign, 4-bit exponent (bias 7), 3-bit mantissa;
+ *     exponent 15 with mantissa 7 is NaN, there is no infinity. The KV cache
+ *     is fp8_e4m3 (sglang PR #11993 "Accelerate deepseek fp4 b200 ci",
+ *     summary of changes).
+ *   - OCP E2M1 nibble: sign, 2-bit exponent (bias 1), 1-bit mantissa.
+ *   - OCP E8M0 byte: 2^(byte-127); 0xFF is NaN.
+ *   The MXFP4 cache is a uint8 tensor with two E2M1 values per byte (ATOM PR
+ *   #1709, commit on the forward_pre split: FP4 is selected by a uint8 kv
+ *   cache). Reading adopted where the pages are silent: the low nibble holds
+ *   the even element, and one E8M0 scale covers 32 consecutive elements. This
+ *   reading is parity unpinned by the pages (only by the round trip against the
+ *   input quantizer).
+ *
+ * Row windows (visible length E_r of query row r):
+ *   - decode with next_n rows per sequence: row r = b*next_n + j sees
+ *     E_r = max(0, len_b - (next_n-1-j)) (reading adopted: the last row of a
+ *     sequence sees the whole context, each earlier row one token less);
+ *   - prefill: E_r = visible_end[r], given per row.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_FP8 1
+#define ORC_MXFP4 2
+
+#define ORC_OK 0
+#define ORC_BAD_ARG 1
+#define ORC_BAD_PAGE 2
+
+/* ---------------------------------------------------------------- decoders */
+
+double orc_dec_fp8_e4m3(uint8_t b)
+{
+    int s = (b >> 7) & 1;
+    int e = (b >> 3) & 15;
+    int m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ((double)m / 8.0) * ldexp(1.0, -6); /* subnormal */
+    else
+        v = (1.0 + (double)m / 8.0) * ldexp(1.0, e - 7);
+    return s ? -v : v;
+}
+
+double orc_dec_e2m1(uint8_t nibble)
+{
+    int s = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 3;
+    int m = nibble & 1;
+    double v;
+    if (e == 0)
+        v = (double)m * 0.5; /* subnormal: 0 or 0.5 */
+    else
+        v = (1.0 + (double)m / 2.0) * ldexp(1.0, e - 1);
+    return s ? -v : v;
+}
+
+double orc_dec_e8m0(uint8_t b)
+{
+    if (b == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+static float orc_load_f32(const uint8_t *p)
+{
+    float f;
+    memcpy(&f, p, sizeof f);
+    return f;
+}
+
+/* ------------------------------------------------------ dequantized operands */
+
+/* Query row r, head h, as D real numbers. FP8: code * per-row fp32 scale (a
+ * null scale means 1). MXFP4: code * e8m0 scale of its 32-element block. */
+static void orc_query_head(int dtype, const uint8_t *q, const uint8_t *q_scale,
+                           int64_t r, int h, int H, int D, double *out)
+{
+    int d;
+    if (dtype == ORC_FP8) {
+        const uint8_t *row = q + ((int64_t)r * H + h) * D;
+        double s = q_scale ? (double)orc_load_f32(q_scale + 4 * r) : 1.0;
+        for (d = 0; d < D; ++d)
+            out[d] = orc_dec_fp8_e4m3(row[d]) * s;
+    } else {
+        const uint8_t *row = q + ((int64_t)r * H + h) * (D / 2);
+        const uint8_t *sc = q_scale + ((int64_t)r * H + h) * (D / 32);
+        for (d = 0; d < D; ++d) {
+            uint8_t byte = row[d / 2];
+            uint8_t nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+            out[d] = orc_dec_e2m1(nib) * orc_dec_e8m0(sc[d / 32]);
+        }
+    }
+}
+
+/* Logical token t of the sequence whose block-table row is bt, as D real
+ * numbers with its stored scale applied. Returns ORC_BAD_PAGE when the
+ * block-table entry is not a page of the pool. */
+static int orc_key_token(int dtype, const uint8_t *kdata, int64_t page_stride,
+                         int64_t row_stride, const uint8_t *kscale,
+                         int64_t scale_page_stride, int64_t scale_row_stride,
+                         int page_size, int64_t num_pages, const int32_t *bt,
+                         int64_t t, int D, double *out)
+{
+    int64_t logical_page = t / page_size;
+    int64_t slot = t % page_size;
+    int64_t phys = bt[logical_page];
+    const uint8_t *row, *srow;
+    int d;
+    if (phys < 0 || phys >= num_pages)
+        return ORC_BAD_PAGE;
+    row = kdata + phys * page_stride + slot * row_stride;
+    srow = kscale + phys * scale_page_stride + slot * scale_row_stride;
+    if (dtype == ORC_FP8) {
+        double s = (double)orc_load_f32(srow);
+        for (d = 0; d < D; ++d)
+            out[d] = orc_dec_fp8_e4m3(row[d]) * s;
+    } else {
+        for (d = 0; d < D; ++d) {
+            uint8_t byte = row[d / 2];
+            uint8_t nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+            out[d] = orc_dec_e2m1(nib) * orc_dec_e8m0(srow[d / 32]);
+        }
+    }
+    return ORC_OK;
+}
+
+/* One logit: sum over heads of w[h] * max(0, q_h . k). */
+static double orc_score(const double *qf /* [H][D] */, const double *kf,
+                        const float *w_row, int H, int D)
+{
+    double logit = 0.0;
+    int h, d;
+    for (h = 0; h < H; ++h) {
+        double s = 0.0;
+        for (d = 0; d < D; ++d)
+            s += qf[(int64_t)h * D + d] * kf[d];
+        if (s > 0.0)
+            logit += (double)w_row[h] * s;
+    }
+    return logit;
+}
+
+/* Scores one query row against tokens [0, E) of the sequence with block-table
+ * row bt; writes out[0..W), with -inf at t >= E. */
+static int orc_row(int dtype, const uint8_t *q, const uint8_t *q_scale,
+                   const float *w, int H, int D, int64_t r, const uint8_t *kdata,
+                   int64_t page_stride, int64_t row_stride, const uint8_t *kscale,
+                   int64_t scale_page_stride, int64_t scale_row_stride,
+                   int page_size, int64_t num_pages, const int32_t *bt, int64_t E,
+                   int64_t W, double *out)
+{
+    double *qf = (double *)malloc(sizeof(double) * (size_t)H * (size_t)D);
+    double *kf = (double *)malloc(sizeof(double) * (size_t)D);
+    int64_t t;
+    int h, rc = ORC_OK;
+    if (!qf || !kf) {
+        free(qf);
+        free(kf);
+        return ORC_BAD_ARG;
+    }
+    for (h = 0; h < H; ++h)
+        orc_query_head(dtype, q, q_scale, r, h, H, D, qf + (int64_t)h * D);
+    for (t = 0; t < W; ++t)
+        out[t] = -INFINITY;
+    for (t = 0; t < E && t < W; ++t) {
+        rc = orc_key_token(dtype, kdata, page_stride, row_stride, kscale,
+                           scale_page_stride, scale_row_stride, page_size,
+                           num_pages, bt, t, D, kf);
+        if (rc != ORC_OK)
+            break;
+        out[t] = orc_score(qf, kf, w + r * H, H, D);
+    }
+    free(qf);
+    free(kf);
+    return rc;
+}
+
+static int orc_check_common(int dtype, int H, int D, int page_size)
+{
+    if (dtype != ORC_FP8 && dtype != ORC_MXFP4)
+        return ORC_BAD_ARG;
+    if (H < 1 || D < 1 || page_size < 1)
+        return ORC_BAD_ARG;
+    if (dtype == ORC_MXFP4 && D % 32 != 0)
+        return ORC_BAD_ARG;
+    return ORC_OK;
+}
+
+/*
+ * Decode: B sequences with next_n query rows each (row r = b*next_n + j).
+ * Computes the listed rows only (rows[i], i < nrows) into out[i][0..W), and
+ * their visible lengths into E_out[i].
+ */
+int orc_decode_logits(int dtype, const uint8_t *q, const uint8_t *q_scale,
+                      const float *w, int H, int D, const uint8_t *kdata,
+                      int64_t page_stride, int64_t row_stride,
+                      const uint8_t *kscale, int64_t scale_page_stride,
+                      int64_t scale_row_stride, int page_size, int64_t num_pages,
+                      const int32_t *block_tables, int64_t bt_stride,
+                      const int32_t *lens, int B, int next_n, const int64_t *rows,
+                      int64_t nrows, int64_t W, double *out, int64_t *E_out)
+{
+    int64_t i;
+    int rc_all = ORC_OK;
+    if (orc_check_common(dtype, H, D, page_size) != ORC_OK || next_n < 1)
+        return ORC_BAD_ARG;
+    for (i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= (int64_t)B * next_n)
+            return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        int64_t b = r / next_n;
+        int64_t j = r % next_n;
+        int64_t E = (int64_t)lens[b] - (next_n - 1 - j);
+        int rc;
+        if (E < 0)
+            E = 0;
+        E_out[i] = E;
+        rc = orc_row(dtype, q, q_scale, w, H, D, r, kdata, page_stride,
+                     row_stride, kscale, scale_page_stride, scale_row_stride,
+                     page_size, num_pages, block_tables + b * bt_stride, E, W,
+                     out + i * W);
+        if (rc != ORC_OK) {
+#pragma omp critical
+            rc_all = rc;
+        }
+    }
+    return rc_all;
+}
+
+/*
+ * Prefill: T query rows of one sequence; row r sees visible_end[r] tokens.
+ * Computes the listed rows only.
+ */
+int orc_prefill_logits(int dtype, const uint8_t *q, const uint8_t *q_scale,
+                       const float *w, int H, int D, const uint8_t *kdata,
+                       int64_t page_stride, int64_t row_stride,
+                       const uint8_t *kscale, int64_t scale_page_stride,
+                       int64_t scale_row_stride, int page_size,
+                       int64_t num_pages, const int32_t *block_table,
+                       const int32_t *visible_end, int64_t T, const int64_t *rows,
+                       int64_t nrows, int64_t W, double *out, int64_t *E_out)
+{
+    int64_t i;
+    int rc_all = ORC_OK;
+    if (orc_check_common(dtype, H, D, page_size) != ORC_OK)
+        return ORC_BAD_ARG;
+    for (i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= T)
+            return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        int64_t E = visible_end[r] < 0 ? 0 : visible_end[r];
+        int rc;
+        E_out[i] = E;
+        rc = orc_row(dtype, q, q_scale, w, H, D, r, kdata, page_stride,
+                     row_stride, kscale, scale_page_stride, scale_row_stride,
+                     page_size, num_pages, block_table, E, W, out + i * W);
+        if (rc != ORC_OK) {
+#pragma omp critical
+            rc_all = rc;
+        }
+    }
+    return rc_all;
+}
+
+/* ------------------------------------------------------------------ top-k */
+
+typedef struct {
+    double v;
+    int64_t t;
+} orc_item;
+
+/* Larger value first; equal values (including -0 against +0, which compare
+ * equal) go to the lower token index first. */
+static int orc_item_cmp(const void *a, const void *b)
+{
+    const orc_item *x = (const orc_item *)a;
+    const orc_item *y = (const orc_item *)b;
+    if (x->v > y->v)
+        return -1;
+    if (x->v < y->v)
+        return 1;
+    if (x->t < y->t)
+        return -1;
+    if (x->t > y->t)
+        return 1;
+    return 0;
+}
+
+static int orc_topk_items(orc_item *items, int64_t E, int k, int32_t *out)
+{
+    int64_t n = E < k ? E : k;
+    int64_t i;
+    qsort(items, (size_t)E, sizeof(orc_item), orc_item_cmp);
+    for (i = 0; i < n; ++i)
+        out[i] = (int32_t)items[i].t;
+    for (i = n; i < k; ++i)
+        out[i] = -1;
+    return ORC_OK;
+}
+
+/* Top-k of one row of double logits v[0..E): token indices, largest first. */
+int orc_topk_f64(const double *v, int64_t E, int k, int32_t *out)
+{
+    orc_item *items;
+    int64_t t;
+    int rc;
+    if (E < 0 || k < 1)
+        return ORC_BAD_ARG;
+    items = (orc_item *)malloc(sizeof(orc_item) * (size_t)(E > 0 ? E : 1));
+    if (!items)
+        return ORC_BAD_ARG;
+    for (t = 0; t < E; ++t) {
+        items[t].v = v[t];
+        items[t].t = t;
+    }
+    rc = orc_topk_items(items, E, k, out);
+    free(items);
+    return rc;
+}
+
+/* Top-k of one row of float logits; the ordering is decided on the float
+ * values themselves (exactly representable in double). */
+int orc_topk_f32(const float *v, int64_t E, int k, int32_t *out)
+{
+    orc_item *items;
+    int64_t t;
+    int rc;
+    if (E < 0 || k < 1)
+        return ORC_BAD_ARG;
+    items = (orc_item *)malloc(sizeof(orc_item) * (size_t)(E > 0 ? E : 1));
+    if (!items)
+        return ORC_BAD_ARG;
+    for (t = 0; t < E; ++t) {
+        items[t].v = (double)v[t];
+        items[t].t = t;
+    }
+    rc = orc_topk_items(items, E, k, out);
+    free(items);
+    return rc;
+}
+
+/* Many rows of float logits (row stride W), each with its own length. */
+int orc_topk_rows_f32(const float *logits, int64_t W, const int64_t *E,
+                      int64_t nrows, int k, int32_t *out)
+{
+    int64_t i;
+    int rc_all = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int rc = orc_topk_f32(logits + i * W, E[i], k, out + i * k);
+        if (rc != ORC_OK) {
+#pragma omp critical
+            rc_all = rc;
+        }
+    }
+    return rc_all;
+}

@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks the oracle against what a library routine, exact rational
+arithmetic, a closed-form special case or an invariant of the definition
+fixes, so that a dropped term, a wrong sign or index, or a transposed operand
+anywhere in the oracle fails at least one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _cache(case):
+    c = case.cache
+    return oracle.Cache(c.dtype, c.data, c.page_stride, c.row_stride, c.scale,
+                        c.scale_page_stride, c.scale_row_stride, c.page_size, c.num_pages)
+
+
+def _decode_all(case, W=None):
+    W = W or case.W
+    rows = np.arange(case.R)
+    return oracle.decode_logits(case.dtype, case.q, case.q_scale, case.w, case.H, case.D,
+                                _cache(case), case.block_tables, case.lens, case.next_n,
+                                rows, W)
+
+
+# ------------------------------------------------------------------ decoders
+
+def test_fp8_decoder_matches_torch_for_all_256_codes():
+    """OCP E4M3FN decoding against torch's float8_e4m3fn -> float32 cast."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.dec_fp8(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e2m1_decoder_matches_ocp_value_table():
+    """The 16 E2M1 codes decode to the OCP MX value set, sign in bit 3."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = [oracle.dec_e2m1(c) for c in range(16)]
+    assert got[:8] == table
+    assert got[8:] == [-v for v in table]
+    assert math.copysign(1.0, got[8]) == -1.0
+
+
+def test_e8m0_decoder_anchor_doubling_and_nan():
+    assert oracle.dec_e8m0(127) == 1.0
+    for b in range(254):
+        assert oracle.dec_e8m0(b + 1) == 2.0 * oracle.dec_e8m0(b)
+    assert math.isnan(oracle.dec_e8m0(255))
+
+
+def test_quantizers_round_trip_through_oracle_decoders():
+    """Input quantizers (synth) and oracle decoders agree on what a code means:
+    dequantized values stay within each format's rounding bound of the input."""
+    rng = synth.rng_for(5)
+    x = rng.standard_normal((64, 128), dtype=np.float32)
+    codes, scale = synth.quantize_fp8_rows(x)
+    dec = np.vectorize(oracle.dec_fp8)(codes) * scale[:, None].astype(np.float64)
+    # E4M3: 3 mantissa bits -> relative error <= 2^-4 for normals; absolute
+    # error <= half the subnormal step (2^-10 * scale) near zero.
+    err = np.abs(dec - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None])
+    assert np.all(err <= bound * (1 + 1e-6))
+    packed, sc = synth.quantize_mxfp4(x)
+    lo = packed & 15
+    hi = packed >> 4
+    nib = np.empty((64, 128), dtype=np.uint8)
+    nib[:, 0::2] = lo
+    nib[:, 1::2] = hi
+    vals = np.vectorize(oracle.dec_e2m1)(nib)
+    s = np.vectorize(oracle.dec_e8m0)(sc)
+    dq = vals * np.repeat(s, 32, axis=1)
+    # block max sits in [4, 8) * 2^e; E2M1 spacing there is 2 * 2^e, so the
+    # error is <= 2^e (half step) everywhere in the block, plus saturation at 6
+    # for values in (6, 8) * 2^e (error < 2 * 2^e).
+    step = np.repeat(s, 32, axis=1)
+    assert np.all(np.abs(dq - x) <= 2.0 * step + 1e-12)
+    assert np.all(np.sign(dq)[np.abs(dq) > 0] == np.sign(x)[np.abs(dq) > 0])
+
+
+# ------------------------------------------------------- exact brute force
+
+def _fp8_exact(code):
+    v = torch.tensor([code], dtype=torch.uint8).view(torch.float8_e4m3fn).float().item()
+    return Fraction(v)
+
+
+def _f32_exact(b4):
+    return Fraction(float(np.frombuffer(bytes(b4), dtype=np.float32)[0]))
+
+
+def _brute_force_decode_fp8(case, r):
+    """Exact rational logits of decode row r: walks the block table by hand."""
+    c = case.cache
+    b, j = divmod(r, case.next_n)
+    E = max(0, int(case.lens[b]) - (case.next_n - 1 - j))
+    qs = Fraction(float(case.q_scale[r]))
+    q = [[_fp8_exact(int(case.q[r, h, d])) * qs for d in range(case.D)]
+         for h in range(case.H)]
+    out = []
+    for t in range(E):
+        page = int(case.block_tables[b, t // c.page_size])
+        slot = t % c.page_size
+        base = page * c.page_stride + slot * c.row_stride
+        if c.scale_offset >= 0:
+            sb = c.scale_offset + page * c.scale_page_stride + slot * c.scale_row_stride
+            ks = _f32_exact(c.data[sb:sb + 4])
+        else:
+            sb = page * c.scale_page_stride + slot * c.scale_row_stride
+            ks = _f32_exact(c.scale[sb:sb + 4])
+        k = [_fp8_exact(int(c.data[base + d])) * ks for d in range(case.D)]
+        total = Fraction(0)
+        for h in range(case.H):
+            s = sum(qa * kb for qa, kb in zip(q[h], k))
+            if s > 0:
+                total += Fraction(float(case.w[r, h])) * s
+        out.append(total)
+    return out
+
+
+@pytest.mark.parametrize("layout,row_stride", [("separate", None), ("row_inline", 144),
+                                               ("page_block", None)])
+def test_oracle_matches_exact_rational_brute_force_fp8(layout, row_stride):
+    case = synth.decode_case([0, 5, 37], next_n=2, P=32, H=3, D=32, k=8, W=40,
+                             layout=layout, row_stride=row_stride, seed=11)
+    got, E = _decode_all(case)
+    for r in range(case.R):
+        exact = _brute_force_decode_fp8(case, r)
+        assert E[r] == len(exact)
+        for t, ex in enumerate(exact):
+            ref = float(ex)
+            assert abs(got[r, t] - ref) <= 1e-12 * max(abs(ref), 1e-30), (r, t)
+        assert np.all(np.isneginf(got[r, len(exact):]))
+
+
+def test_oracle_mxfp4_matches_exact_rational_brute_force():
+    case = synth.decode_case([3, 33], next_n=1, P=32, H=2, D=64, k=4, dtype=synth.MXFP4,
+                             seed=12)
+    got, E = _decode_all(case)
+    c = case.cache
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+    def nib_val(n):
+        v = Fraction(table[n & 7])
+        return -v if n & 8 else v
+
+    for r in range(case.R):
+        q = []
+        for h in range(case.H):
+            row = []
+            for d in range(case.D):
+                byte = int(case.q[r, h, d // 2])
+                n = byte & 15 if d % 2 == 0 else byte >> 4
+                row.append(nib_val(n) * Fraction(2) ** (int(case.q_scale[r, h, d // 32]) - 127))
+            q.append(row)
+        for t in range(int(E[r])):
+            page = int(case.block_tables[r, t // c.page_size])
+            base = page * c.page_stride + (t % c.page_size) * c.row_stride
+            sb = page * c.scale_page_stride + (t % c.page_size) * c.scale_row_stride
+            k = []
+            for d in range(case.D):
+                byte = int(c.data[base + d // 2])
+                n = byte & 15 if d % 2 == 0 else byte >> 4
+                k.append(nib_val(n) * Fraction(2) ** (int(c.scale[sb + d // 32]) - 127))
+            ex = Fraction(0)
+            for h in range(case.H):
+                s = sum(a * b for a, b in zip(q[h], k))
+                if s > 0:
+                    ex += Fraction(float(case.w[r, h])) * s
+            assert abs(got[r, t] - float(ex)) <= 1e-12 * max(abs(float(ex)), 1e-30)
+
+
+# -------------------------------------------- special cases and invariants
+
+def _dense_keys_fp8(case, b):
+    """Logical keys of sequence b, dequantized through torch's FP8 cast and
+    gathered with numpy indexing (a path independent of the oracle's walk)."""
+    c = case.cache
+    P = c.page_size
+    L = int(case.lens[b])
+    pages = case.block_tables[b, :(L + P - 1) // P].astype(np.int64)
+    rows = (pages[:, None] * P + np.arange(P)).reshape(-1)[:L]
+    data = c.data.reshape(c.num_pages * P, c.row_stride)[rows, :case.D]
+    kf = torch.from_numpy(np.ascontiguousarray(data)).view(torch.float8_e4m3fn).double().numpy()
+    ks = c.scale.view(np.float32)[rows].astype(np.float64)
+    return kf * ks[:, None]
+
+
+def test_single_head_unit_weight_reduces_to_relu_matvec():
+    """H=1, w=1: logits = max(0, K q) (numpy matmul on torch-decoded values)."""
+    case = synth.decode_case([70, 1, 128], next_n=1, P=32, H=1, D=128, k=4, seed=21)
+    case.w[:] = 1.0
+    got, E = _decode_all(case)
+    for b in range(case.B):
+        kf = _dense_keys_fp8(case, b)
+        qf = torch.from_numpy(case.q[b, 0].copy()).view(torch.float8_e4m3fn).double().numpy()
+        qf = qf * float(case.q_scale[b])
+        ref = np.maximum(kf @ qf, 0.0)
+        assert np.allclose(got[b, :E[b]], ref, rtol=1e-13, atol=0)
+
+
+def test_identical_heads_with_mean_weights_equal_single_head():
+    """All heads equal and w = 1/H gives exactly the single-head relu(K q)
+    (up to double rounding)."""
+    case = synth.decode_case([90], next_n=1, P=32, H=8, D=128, k=4, seed=22)
+    case.q[:, 1:] = case.q[:, :1]
+    case.w[:] = 1.0 / 8.0
+    got, E = _decode_all(case)
+    kf = _dense_keys_fp8(case, 0)
+    qf = torch.from_numpy(case.q[0, 0].copy()).view(torch.float8_e4m3fn).double().numpy()
+    ref = np.maximum(kf @ (qf * float(case.q_scale[0])), 0.0)
+    assert np.allclose(got[0, :E[0]], ref, rtol=1e-12, atol=0)
+
+
+def test_multi_head_matches_dense_matmul_formulation():
+    """Paged oracle vs a dense numpy formulation relu(Q K^T) w on gathered keys."""
+    case = synth.decode_case([200, 64, 33], next_n=2, P=32, H=16, D=128, k=8, seed=23)
+    got, E = _decode_all(case)
+    for r in range(case.R):
+        b = r // 2
+        kf = _dense_keys_fp8(case, b)
+        qf = torch.from_numpy(case.q[r].copy()).view(torch.float8_e4m3fn).double().numpy()
+        qf = qf * float(case.q_scale[r])
+        S = qf @ kf.T                                  # [H, L]
+        ref = (np.maximum(S, 0.0) * case.w[r].astype(np.float64)[:, None]).sum(axis=0)
+        e = int(E[r])
+        assert e == max(0, int(case.lens[b]) - (1 - r % 2))
+        scale = max(np.abs(ref[:e]).max() if e else 1.0, 1e-30)
+        assert np.max(np.abs(got[r, :e] - ref[:e]), initial=0.0) <= 1e-12 * scale
+
+
+def test_physical_page_permutation_is_invisible():
+    case = synth.decode_case([100, 77], next_n=1, P=32, H=4, D=128, k=8, seed=24,
+                             pool_pages=20)
+    base, _ = _decode_all(case)
+    c = case.cache
+    perm = np.random.default_rng(3).permutation(c.num_pages)
+    pages = c.data.reshape(c.num_pages, -1)
+    spages = c.scale.reshape(c.num_pages, -1)
+    new_data = np.empty_like(pages)
+    new_scale = np.empty_like(spages)
+    new_data[perm] = pages
+    new_scale[perm] = spages
+    c.data = new_data.reshape(-1)
+    c.scale = new_scale.reshape(-1)
+    bt = case.block_tables.copy()
+    used = bt != synth.BT_SENTINEL
+    bt[used] = perm[bt[used]]
+    case.block_tables = bt
+    moved, _ = _decode_all(case)
+    assert np.array_equal(base, moved)
+
+
+def test_canaries_and_sentinels_never_reach_visible_logits():
+    """NaN canaries in tail slots/unreferenced pages and sentinels in unused
+    block-table entries leave every visible logit finite and unchanged."""
+    a = synth.decode_case([45, 3, 64], next_n=2, P=32, H=4, D=128, k=8, seed=25, canary=True)
+    b = synth.decode_case([45, 3, 64], next_n=2, P=32, H=4, D=128, k=8, seed=25, canary=False)
+    la, Ea = _decode_all(a)
+    lb, Eb = _decode_all(b)
+    assert np.array_equal(Ea, Eb)
+    for r in range(a.R):
+        assert np.all(np.isfinite(la[r, :Ea[r]]))
+    assert np.array_equal(la, lb)
+
+
+def test_mtp_rows_equal_single_row_calls_with_shorter_lengths():
+    case = synth.decode_case([50, 1, 0], next_n=3, P=32, H=4, D=128, k=8, seed=26)
+    got, E = _decode_all(case)
+    for r in range(case.R):
+        b, j = divmod(r, 3)
+        one = synth.decode_case([50, 1, 0], next_n=3, P=32, H=4, D=128, k=8, seed=26)
+        one.lens = np.maximum(case.lens - (3 - 1 - j), 0).astype(np.int32)
+        one.next_n = 1
+        one.q = case.q[j::3].copy()
+        one.q_scale = case.q_scale[j::3].copy()
+        one.w = case.w[j::3].copy()
+        ref, Er = oracle.decode_logits(one.dtype, one.q, one.q_scale, one.w, one.H, one.D,
+                                       _cache(one), one.block_tables, one.lens, 1, [b], case.W)
+        assert Er[0] == E[r]
+        assert np.array_equal(ref[0], got[r])
+
+
+def test_key_scale_doubling_and_weight_negation_are_exact():
+    case = synth.decode_case([60], next_n=1, P=32, H=4, D=128, k=8, seed=27, canary=False)
+    base, E = _decode_all(case)
+    case.cache.scale = (case.cache.scale.view(np.float32) * np.float32(2)).view(np.uint8)
+    doubled, _ = _decode_all(case)
+    assert np.array_equal(doubled[0, :E[0]], 2 * base[0, :E[0]])
+    case.cache.scale = (case.cache.scale.view(np.float32) / np.float32(2)).view(np.uint8)
+    case.w = -case.w
+    neg, _ = _decode_all(case)
+    assert np.array_equal(neg[0, :E[0]], -base[0, :E[0]])
+
+
+def test_mxfp4_scale_byte_increment_doubles_logits():
+    case = synth.decode_case([40], next_n=1, P=32, H=2, D=128, k=8, dtype=synth.MXFP4,
+                             seed=28, canary=False)
+    base, E = _decode_all(case)
+    case.cache.scale = (case.cache.scale + 1).astype(np.uint8)
+    got, _ = _decode_all(case)
+    assert np.array_equal(got[0, :E[0]], 2 * base[0, :E[0]])
+
+
+def test_empty_history_gives_no_logits_and_no_selection():
+    case = synth.decode_case([0, 0], next_n=2, P=32, H=4, D=128, k=8, W=16, seed=29)
+    got, E = _decode_all(case)
+    assert np.all(E == 0) and np.all(np.isneginf(got))
+    assert np.all(oracle.topk(got[0], 0, 8) == -1)
+
+
+def test_prefill_rows_match_decode_rows_of_same_keys():
+    """A prefill row with visible_end e scores exactly like a one-row decode of
+    the same keys with length e."""
+    pc = synth.prefill_case(40, 96, P=32, H=4, D=128, k=8, seed=30)
+    rows = np.arange(pc.T)
+    got, E = oracle.prefill_logits(pc.dtype, pc.q, pc.q_scale, pc.w, pc.H, pc.D,
+                                   _cache(pc), pc.block_table, pc.visible_end, rows, pc.W)
+    assert np.array_equal(E, np.minimum((rows + 1) // 4, 96))
+    bt = pc.block_table[None, :]
+    for r in (0, 3, 7, 39):
+        ref, Er = oracle.decode_logits(pc.dtype, pc.q[r:r + 1], pc.q_scale[r:r + 1],
+                                       pc.w[r:r + 1], pc.H, pc.D, _cache(pc), bt,
+                                       np.array([pc.visible_end[r]]), 1, [0], pc.W)
+        assert Er[0] == E[r]
+        assert np.array_equal(ref[0], got[r])
+
+
+# ------------------------------------------------------------------- top-k
+
+def _lexsort_topk(v, E, k):
+    idx = np.lexsort((np.arange(E), -v[:E].astype(np.float64)))
+    out = np.full(k, -1, dtype=np.int32)
+    n = min(k, E)
+    out[:n] = idx[:n]
+    return out
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (5, 8), (100, 7), (1000, 64), (4096, 512)])
+def test_topk_matches_numpy_lexsort(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    v = rng.standard_normal(E).astype(np.float32)
+    v[rng.integers(0, E, size=E // 4)] = v[0]  # plant ties
+    got = oracle.topk(v, E, k)
+    assert np.array_equal(got, _lexsort_topk(v, E, k))
+    sel = got[got >= 0]
+    rest = np.setdiff1d(np.arange(E), sel)
+    if len(rest) and len(sel):
+        assert v[sel].min() >= v[rest].max()
+
+
+def test_topk_ties_go_to_lower_index_and_signed_zeros_are_equal():
+    v = np.array([0.0, -0.0, 1.0, 0.0, -0.0, 1.0, -1.0], dtype=np.float32)
+    got = oracle.topk(v, 7, 4)
+    assert list(got) == [2, 5, 0, 1]
+    v2 = np.full(10, 3.5, dtype=np.float32)
+    assert list(oracle.topk(v2, 10, 3)) == [0, 1, 2]
+
+
+def test_topk_pads_with_minus_one_when_row_is_short():
+    v = np.array([2.0, 1.0, 3.0], dtype=np.float32)
+    assert list(oracle.topk(v, 3, 6)) == [2, 0, 1, -1, -1, -1]
+    assert list(oracle.topk(v, 0, 2)) == [-1, -1]
+
+
+def test_topk_rows_f32_matches_per_row():
+    rng = np.random.default_rng(9)
+    lg = rng.standard_normal((5, 300)).astype(np.float32)
+    E = np.array([0, 1, 299, 300, 150])
+    out = oracle.topk_rows_f32(lg, E, 16)
+    for i in range(5):
+        assert np.array_equal(out[i], _lexsort_topk(lg[i], E[i], 16))
