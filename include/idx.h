@@ -1,0 +1,229 @@
+/*
+ * idx.h — C ABI of the MI355X (gfx950) sparse-attention indexer library.
+ *
+ * The library computes, for every query row of a batch, the indexer scores
+ *     logits[r][t] = sum_h w[r][h] * max(0, k_scale[t] * (q[r][h] . k[t]))
+ * over a single-head K cache stored in fixed-size physical pages, and then the
+ * row's top-k token indices. The pages this is built from name the op
+ * "mqa-logits" followed by "indexer_score_topk" (ROCm/ATOM PR #1709 "Add fp4
+ * indexer fo dsv4": commit on the single-kernel varctx schedule, commit on the
+ * forward_pre / score_topk_from split, commit on right-sizing the prefill
+ * logits; vllm-project/DeepGEMM PR #14: summary, "FP8 paged-MQA logits").
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are device pointers unless the comment says "host".
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronizes; work is enqueued asynchronously on `stream` (a
+ *     hipStream_t; NULL is the default stream). No call makes a hidden
+ *     device-to-host copy, so every entry point can be captured into a HIP
+ *     graph (flashinfer PR #3269, review discussion on .item() syncs in the
+ *     DSv4 sparse-MLA input checks).
+ *   - Argument errors are reported as an idx_status, never by aborting
+ *     (flashinfer PR #3269, review: validate with explicit errors, not
+ *     asserts). The message of the last failure on the calling thread is in
+ *     idx_last_error(). Host-side checks run before any HIP call, so a
+ *     rejected call touches no device state.
+ *   - Device-side contracts that cannot be checked without a sync
+ *     (len <= W, block-table entries of visible tokens naming pages of the
+ *     pool) are not checked; K loads are bounds-checked against the pool so a
+ *     bad page id reads zeros instead of faulting (ATOM PR #1709, commit on
+ *     the ragged-window refresh: a bounds-check-off buffer load turned stale
+ *     metadata into a memory fault).
+ *   - Supported shapes: num_heads = 64, head_dim = 128, page_size in
+ *     {32, 64, 256}, next_n in [1, 4], top-k row width W <= 65536.
+ *
+ * Thread safety: calls are stateless apart from the thread-local error
+ * string; concurrent calls on different streams are safe.
+ */
+#ifndef IDX_H_
+#define IDX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum idx_status {
+    IDX_OK = 0,
+    IDX_ERR_INVALID = 1,     /* bad pointer, size, stride or alignment */
+    IDX_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    IDX_ERR_WORKSPACE = 3,   /* caller-provided buffer too small */
+    IDX_ERR_HIP = 4          /* a HIP runtime call failed */
+} idx_status;
+
+/* Element formats of q and of the K cache. FP8 is OCP E4M3FN (the cache is
+ * fp8_e4m3: sglang PR #11993, summary of changes). MXFP4 is OCP E2M1, two
+ * values per byte with the even element in the low nibble, plus one E8M0
+ * scale byte per 32 consecutive elements; a uint8 cache selects it (ATOM PR
+ * #1709, commit on the forward_pre split). */
+typedef enum idx_dtype {
+    IDX_FP8_E4M3 = 1,
+    IDX_MXFP4 = 2
+} idx_dtype;
+
+/* Query rows. R rows, H heads, head dim D.
+ *   FP8:   q       bytes [R][H][D]
+ *          q_scale fp32  [R] (one scale per token), or NULL meaning 1
+ *   MXFP4: q       bytes [R][H][D/2]
+ *          q_scale E8M0  [R][H][D/32] (required)
+ *   weights fp32 [R][H] (per-row, per-head indexer weights; any sign).
+ * q must be 16-byte aligned. */
+typedef struct idx_query {
+    int32_t dtype;     /* idx_dtype */
+    int32_t num_heads; /* H; must be 64 */
+    int32_t head_dim;  /* D; must be 128 */
+    int32_t reserved;  /* set to 0 */
+    const void *q;
+    const void *q_scale;
+    const float *weights;
+} idx_query;
+
+/* Paged single-head K cache. Token slot s of physical page p:
+ *   data row  at data  + p*page_stride_bytes       + s*row_stride_bytes
+ *   its scale at scale + p*scale_page_stride_bytes + s*scale_row_stride_bytes
+ * FP8 rows hold D bytes and the scale is one fp32; MXFP4 rows hold D/2 bytes
+ * and the scale is D/32 E8M0 bytes. The two stride pairs express a separate
+ * scale array, scales interleaved in a padded row (e.g. 144-byte rows) and
+ * per-page [P rows][P scales] blocks (DeepGEMM PR #14 summary: padded page
+ * strides; fused-cache API). Data rows must be 16-byte aligned (data,
+ * page_stride_bytes, row_stride_bytes multiples of 16); scale addresses
+ * 4-byte aligned. num_pages bounds every K load. */
+typedef struct idx_kv_cache {
+    int32_t dtype;     /* idx_dtype; must equal the query dtype */
+    int32_t page_size; /* P: 32, 64 or 256 */
+    int64_t num_pages;
+    const void *data;
+    int64_t page_stride_bytes;
+    int64_t row_stride_bytes;
+    const void *scale;
+    int64_t scale_page_stride_bytes;
+    int64_t scale_row_stride_bytes;
+} idx_kv_cache;
+
+/* Number of int32 entries of a schedule buffer for n_ctas work groups. */
+int64_t idx_schedule_ints(int32_t n_ctas);
+
+/* Number of work groups a schedule should be built for on this device
+ * when the batch has `rows` query rows (host only; queries the current
+ * device once). Returns a positive count, or 0 when no device is present. */
+int32_t idx_recommended_ctas(int32_t rows);
+
+/*
+ * Build the decode work split (ATOM PR #1709, commit on compute_varctx_schedule:
+ * one kernel writes the split straight into a fixed-address buffer that a
+ * captured graph reads, replacing many small launches). Sequence b holds
+ * ceil(context_lens[b] / BK) blocks of BK = min(page_size, 64) tokens, so no
+ * block straddles two pages (DeepGEMM PR #14: BLOCK_KV = min(PAGE_KV, 64), a
+ * tile must not span two non-contiguous pages). The blocks of all sequences,
+ * in order, are split into n_ctas contiguous, near-equal ranges.
+ *
+ *   context_lens  int32 [B], device; read at kernel time (so a graph replay
+ *                 sees the lengths current at replay)
+ *   cta_info      int32 [idx_schedule_ints(n_ctas)], device, written: entry c
+ *                 holds the (sequence, block) where work group c starts; entry
+ *                 n_ctas holds the end (B, 0).
+ * Errors: IDX_ERR_INVALID for null pointers, B < 1 or B > 16000,
+ * next_n outside [1,4], page_size not 32/64/256, n_ctas < 1 or > 1<<20.
+ */
+idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t next_n,
+                              int32_t page_size, int32_t n_ctas, int32_t *cta_info,
+                              void *stream);
+
+/*
+ * Decode scores ("mqa-logits"). Query row r = b*next_n + j (j < next_n) of
+ * sequence b sees E_r = max(0, context_lens[b] - (next_n - 1 - j)) tokens;
+ * for t < E_r it writes logits[r*W + t]. Columns t >= E_r are not written.
+ *
+ *   q, kv          descriptors above (host pointers to structs holding
+ *                  device pointers); kv->dtype == q->dtype
+ *   block_tables   int32 [B][bt_stride]; entry i of row b is the physical page
+ *                  of tokens [i*P, (i+1)*P); only entries < ceil(len_b / P)
+ *                  are read
+ *   cta_info       schedule from idx_build_schedule with the same lens, B,
+ *                  next_n, page_size and n_ctas (required)
+ *   logits         fp32 [B*next_n][W]
+ * Errors: IDX_ERR_INVALID (null pointer, shape, alignment, W < 1),
+ * IDX_ERR_UNSUPPORTED (H != 64, D != 128, dtype mismatch).
+ */
+idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
+                                const int32_t *block_tables, int64_t bt_stride,
+                                const int32_t *context_lens, int32_t B, int32_t next_n,
+                                const int32_t *cta_info, int32_t n_ctas, float *logits,
+                                int64_t W, void *stream);
+
+/* Workspace bytes idx_topk needs for `rows` rows of width W (0 for W <= 65536). */
+size_t idx_topk_workspace_size(int32_t rows, int64_t W, int32_t k);
+
+/*
+ * Per-row top-k ("indexer_score_topk"). Row r = b*next_n + j has E_r as in
+ * idx_paged_mqa_logits and reads logits[r*W + t] for t < E_r only. It writes
+ * the min(k, E_r) token indices with the largest logits to
+ * out_idx[r*k .. r*k + k), in ascending index order, padded with -1; equal
+ * logits are taken lowest index first, and -0.0 equals +0.0. Indices are
+ * sequence-local (ATOM PR #1709, commit on the prefill width: the FP4 path
+ * emits seq-local indices). out_count[r] = min(k, E_r) when out_count is not
+ * NULL. Logits must be finite for t < E_r.
+ * Errors: IDX_ERR_INVALID (null pointer, k < 1, W < 1),
+ * IDX_ERR_UNSUPPORTED (W > 65536), IDX_ERR_WORKSPACE (ws_bytes below
+ * idx_topk_workspace_size).
+ */
+idx_status idx_topk(const float *logits, int64_t W, const int32_t *context_lens, int32_t B,
+                    int32_t next_n, int32_t k, int32_t *out_idx, int32_t *out_count,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Rows per prefill chunk for width W under a logits budget of budget_bytes:
+ * max(1, floor(budget_bytes / (4*W))) (host only). */
+int64_t idx_prefill_rows_per_chunk(int64_t W, int64_t budget_bytes);
+
+/* Logits scratch bytes idx_prefill_chunked_topk needs: 4*W*min(T, rows per
+ * chunk) (host only). */
+int64_t idx_prefill_scratch_bytes(int32_t T, int64_t W, int64_t budget_bytes);
+
+/* int32 entries of cta_scratch idx_prefill_chunked_topk needs. */
+int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes);
+
+/*
+ * Prefill: scores and top-k of T query rows of one sequence against its
+ * committed keys, in query-row chunks whose fp32 logits stay within
+ * budget_bytes (ATOM PR #1709, commit on right-sizing the prefill logits:
+ * the width is the batch's actual maximum committed length, known on the
+ * host without a device sync, and Q-row budget chunking rebuilds the
+ * schedule per chunk because it encodes absolute row ids). Row r sees
+ * visible_end[r] tokens. The result does not depend on budget_bytes.
+ *
+ *   block_table    int32 [ceil(max visible_end / P)] physical pages of the
+ *                  sequence
+ *   visible_end    int32 [T], device
+ *   W              host: logits width, >= every visible_end[r] (the
+ *                  right-sized width max_r visible_end[r])
+ *   logits_scratch fp32, scratch_bytes >= idx_prefill_scratch_bytes(T, W, budget)
+ *   cta_scratch    int32, cta_scratch_ints >= idx_prefill_schedule_ints(...)
+ *   out_idx        int32 [T][k], seq-local indices as in idx_topk
+ * The host loop over chunks enqueues schedule, scores and top-k per chunk on
+ * `stream` without synchronizing.
+ * Errors: as idx_paged_mqa_logits and idx_topk; IDX_ERR_WORKSPACE when a
+ * scratch buffer is too small.
+ */
+idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
+                                    const int32_t *block_table, const int32_t *visible_end,
+                                    int32_t T, int64_t W, int64_t budget_bytes, int32_t k,
+                                    float *logits_scratch, int64_t scratch_bytes,
+                                    int32_t *cta_scratch, int64_t cta_scratch_ints,
+                                    int32_t *out_idx, void *stream);
+
+/* Human-readable name of a status (static string). */
+const char *idx_status_string(idx_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *idx_last_error(void);
+
+/* ABI version of this library (major*10000 + minor*100 + patch). */
+int32_t idx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H_ */

@@ -1,0 +1,339 @@
+// C ABI of the indexer library: host-side validation and kernel dispatch.
+// Every check here runs before any HIP call, so a rejected call leaves the
+// device untouched; nothing here allocates, frees or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+idx_status fail(idx_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+idx_status ok() {
+  g_last_error[0] = '\0';
+  return IDX_OK;
+}
+
+idx_status hip_fail(hipError_t e, const char *what) {
+  return fail(IDX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_page_size(int32_t p) { return p == 32 || p == 64 || p == 256; }
+
+constexpr int32_t kMaxCtas = 1 << 20;
+
+idx_status check_query(const idx_query *q) {
+  if (!q) return fail(IDX_ERR_INVALID, "query descriptor is null");
+  if (q->dtype != IDX_FP8_E4M3 && q->dtype != IDX_MXFP4)
+    return fail(IDX_ERR_UNSUPPORTED, "query dtype %d is not FP8_E4M3 (1) or MXFP4 (2)", q->dtype);
+  if (q->num_heads != idx::kHeads)
+    return fail(IDX_ERR_UNSUPPORTED, "num_heads %d unsupported (64 only)", q->num_heads);
+  if (q->head_dim != idx::kHeadDim)
+    return fail(IDX_ERR_UNSUPPORTED, "head_dim %d unsupported (128 only)", q->head_dim);
+  if (!q->q || !q->weights) return fail(IDX_ERR_INVALID, "q or weights pointer is null");
+  if (!aligned(q->q, 16)) return fail(IDX_ERR_INVALID, "q must be 16-byte aligned");
+  if (!aligned(q->weights, 16)) return fail(IDX_ERR_INVALID, "weights must be 16-byte aligned");
+  if (q->dtype == IDX_MXFP4 && !q->q_scale)
+    return fail(IDX_ERR_INVALID, "MXFP4 queries need their E8M0 scales (q_scale)");
+  if (q->dtype == IDX_FP8_E4M3 && q->q_scale && !aligned(q->q_scale, 4))
+    return fail(IDX_ERR_INVALID, "FP8 q_scale must be 4-byte aligned");
+  return IDX_OK;
+}
+
+idx_status check_cache(const idx_kv_cache *kv, int32_t dtype) {
+  if (!kv) return fail(IDX_ERR_INVALID, "kv cache descriptor is null");
+  if (kv->dtype != dtype)
+    return fail(IDX_ERR_UNSUPPORTED, "kv dtype %d differs from query dtype %d", kv->dtype, dtype);
+  if (!valid_page_size(kv->page_size))
+    return fail(IDX_ERR_INVALID, "page_size %d not in {32, 64, 256}", kv->page_size);
+  if (!kv->data || !kv->scale) return fail(IDX_ERR_INVALID, "kv data or scale pointer is null");
+  if (kv->num_pages < 1) return fail(IDX_ERR_INVALID, "num_pages must be >= 1");
+  const int64_t row_bytes = dtype == IDX_FP8_E4M3 ? idx::kHeadDim : idx::kHeadDim / 2;
+  if (!aligned(kv->data, 16) || kv->row_stride_bytes % 16 || kv->page_stride_bytes % 16)
+    return fail(IDX_ERR_INVALID, "kv data pointer and strides must be multiples of 16 bytes");
+  if (kv->row_stride_bytes < row_bytes)
+    return fail(IDX_ERR_INVALID, "row_stride_bytes %lld below the %lld-byte row",
+                (long long)kv->row_stride_bytes, (long long)row_bytes);
+  if (kv->page_stride_bytes < (int64_t)(kv->page_size - 1) * kv->row_stride_bytes + row_bytes)
+    return fail(IDX_ERR_INVALID, "page_stride_bytes too small for page_size rows");
+  if ((int64_t)kv->page_size * kv->row_stride_bytes >= (1ll << 31))
+    return fail(IDX_ERR_INVALID, "page extent must stay below 2 GiB");
+  if (!aligned(kv->scale, 4) || kv->scale_row_stride_bytes % 4 || kv->scale_page_stride_bytes % 4)
+    return fail(IDX_ERR_INVALID, "kv scale pointer and strides must be multiples of 4 bytes");
+  if (kv->scale_row_stride_bytes < 4)
+    return fail(IDX_ERR_INVALID, "scale_row_stride_bytes must be >= 4");
+  if ((int64_t)kv->page_size * kv->scale_row_stride_bytes >= (1ll << 31))
+    return fail(IDX_ERR_INVALID, "scale page extent must stay below 2 GiB");
+  return IDX_OK;
+}
+
+idx::LogitsArgs logits_args(const idx_query *q, const idx_kv_cache *kv) {
+  idx::LogitsArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint8_t *>(q->q);
+  a.q_scale = static_cast<const uint8_t *>(q->q_scale);
+  a.weights = q->weights;
+  a.kdata = static_cast<const uint8_t *>(kv->data);
+  a.page_stride = kv->page_stride_bytes;
+  a.row_stride = kv->row_stride_bytes;
+  a.kscale = static_cast<const uint8_t *>(kv->scale);
+  a.scale_page_stride = kv->scale_page_stride_bytes;
+  a.scale_row_stride = kv->scale_row_stride_bytes;
+  a.num_pages = kv->num_pages;
+  a.page_size = kv->page_size;
+  a.block_tokens = idx::block_tokens(kv->page_size);
+  return a;
+}
+
+int64_t prefill_rows_per_chunk(int64_t W, int64_t budget) {
+  int64_t rows = budget / (4 * W);
+  return rows < 1 ? 1 : rows;
+}
+
+// Rows of one prefill chunk actually used: the budget rule, capped so the
+// schedule builder's segment scan fits in LDS (the result does not depend on
+// the chunking).
+int64_t prefill_chunk_rows(int32_t T, int64_t W, int64_t budget) {
+  int64_t rows = prefill_rows_per_chunk(W, budget);
+  const int64_t cap = (int64_t)idx::kMaxSegs * idx::kPrefillRowsPerSeg;
+  if (rows > cap) rows = cap;
+  if (rows > T) rows = T;
+  return rows < 1 ? 1 : rows;
+}
+
+// Work groups of a prefill chunk: one per pair of query rows, at most 8192.
+int32_t prefill_ctas(int64_t chunk_rows) {
+  int64_t segs = (chunk_rows + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg;
+  if (segs < 1) segs = 1;
+  return (int32_t)(segs < 8192 ? segs : 8192);
+}
+
+} // namespace
+
+extern "C" {
+
+int32_t idx_version(void) { return 100; }
+
+const char *idx_status_string(idx_status s) {
+  switch (s) {
+  case IDX_OK: return "IDX_OK";
+  case IDX_ERR_INVALID: return "IDX_ERR_INVALID";
+  case IDX_ERR_UNSUPPORTED: return "IDX_ERR_UNSUPPORTED";
+  case IDX_ERR_WORKSPACE: return "IDX_ERR_WORKSPACE";
+  case IDX_ERR_HIP: return "IDX_ERR_HIP";
+  }
+  return "IDX_ERR_UNKNOWN";
+}
+
+const char *idx_last_error(void) { return g_last_error; }
+
+int64_t idx_schedule_ints(int32_t n_ctas) { return n_ctas < 1 ? 0 : 2 * ((int64_t)n_ctas + 1); }
+
+int32_t idx_recommended_ctas(int32_t rows) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  int64_t n = (int64_t)cus * 8;
+  if (rows > n) n = rows;
+  return (int32_t)(n < kMaxCtas ? n : kMaxCtas);
+}
+
+idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t next_n,
+                              int32_t page_size, int32_t n_ctas, int32_t *cta_info,
+                              void *stream) {
+  if (!context_lens || !cta_info) return fail(IDX_ERR_INVALID, "null context_lens or cta_info");
+  if (B < 1 || B > idx::kMaxSegs)
+    return fail(IDX_ERR_INVALID, "B = %d outside [1, %d]", B, idx::kMaxSegs);
+  if (next_n < 1 || next_n > 4) return fail(IDX_ERR_INVALID, "next_n = %d outside [1, 4]", next_n);
+  if (!valid_page_size(page_size))
+    return fail(IDX_ERR_INVALID, "page_size %d not in {32, 64, 256}", page_size);
+  if (n_ctas < 1 || n_ctas > kMaxCtas)
+    return fail(IDX_ERR_INVALID, "n_ctas = %d outside [1, %d]", n_ctas, kMaxCtas);
+  idx::ScheduleArgs a;
+  a.lens = context_lens;
+  a.nseg = B;
+  a.mode = idx::kSegDecode;
+  a.row0 = 0;
+  a.row_end = 0;
+  a.block_tokens = idx::block_tokens(page_size);
+  a.n_ctas = n_ctas;
+  a.cta_info = cta_info;
+  hipError_t e = idx::launch_schedule(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "schedule launch");
+  return ok();
+}
+
+idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
+                                const int32_t *block_tables, int64_t bt_stride,
+                                const int32_t *context_lens, int32_t B, int32_t next_n,
+                                const int32_t *cta_info, int32_t n_ctas, float *logits,
+                                int64_t W, void *stream) {
+  idx_status st = check_query(q);
+  if (st != IDX_OK) return st;
+  if ((st = check_cache(kv, q->dtype)) != IDX_OK) return st;
+  if (!block_tables || !context_lens || !cta_info || !logits)
+    return fail(IDX_ERR_INVALID, "null block_tables, context_lens, cta_info or logits");
+  if (B < 1 || B > idx::kMaxSegs)
+    return fail(IDX_ERR_INVALID, "B = %d outside [1, %d]", B, idx::kMaxSegs);
+  if (next_n < 1 || next_n > 4) return fail(IDX_ERR_INVALID, "next_n = %d outside [1, 4]", next_n);
+  if (bt_stride < 1) return fail(IDX_ERR_INVALID, "bt_stride must be >= 1");
+  if (n_ctas < 1 || n_ctas > kMaxCtas)
+    return fail(IDX_ERR_INVALID, "n_ctas = %d outside [1, %d]", n_ctas, kMaxCtas);
+  if (W < 1 || W > (1ll << 31)) return fail(IDX_ERR_INVALID, "W = %lld outside [1, 2^31]", (long long)W);
+  idx::LogitsArgs a = logits_args(q, kv);
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.bt_cols = bt_stride;
+  a.lens = context_lens;
+  a.nseg = B;
+  a.next_n = next_n;
+  a.cta_info = cta_info;
+  a.n_ctas = n_ctas;
+  a.logits = logits;
+  a.W = W;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = q->dtype == IDX_FP8_E4M3 ? idx::launch_logits_fp8_decode(a, s)
+                                          : idx::launch_logits_mxfp4_decode(a, s);
+  if (e != hipSuccess) return hip_fail(e, "logits launch");
+  return ok();
+}
+
+size_t idx_topk_workspace_size(int32_t rows, int64_t W, int32_t k) {
+  (void)rows;
+  (void)W;
+  (void)k;
+  return 0;
+}
+
+idx_status idx_topk(const float *logits, int64_t W, const int32_t *context_lens, int32_t B,
+                    int32_t next_n, int32_t k, int32_t *out_idx, int32_t *out_count, void *ws,
+                    size_t ws_bytes, void *stream) {
+  (void)ws;
+  if (!logits || !context_lens || !out_idx)
+    return fail(IDX_ERR_INVALID, "null logits, context_lens or out_idx");
+  if (B < 1) return fail(IDX_ERR_INVALID, "B must be >= 1");
+  if (next_n < 1 || next_n > 4) return fail(IDX_ERR_INVALID, "next_n = %d outside [1, 4]", next_n);
+  if (W < 1) return fail(IDX_ERR_INVALID, "W must be >= 1");
+  if (k < 1) return fail(IDX_ERR_INVALID, "k = %d must be >= 1", k);
+  if (W > idx::kTopkMaxW)
+    return fail(IDX_ERR_UNSUPPORTED, "W = %lld above the %d-wide in-register top-k", (long long)W,
+                idx::kTopkMaxW);
+  if ((int64_t)B * next_n > (1ll << 31) - 1) return fail(IDX_ERR_INVALID, "too many rows");
+  if (ws_bytes < idx_topk_workspace_size(B * next_n, W, k))
+    return fail(IDX_ERR_WORKSPACE, "top-k workspace too small");
+  idx::TopkArgs a;
+  a.logits = logits;
+  a.W = W;
+  a.lens = context_lens;
+  a.next_n = next_n;
+  a.R = B * next_n;
+  a.k = k;
+  a.out_idx = out_idx;
+  a.out_count = out_count;
+  hipError_t e = idx::launch_topk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+int64_t idx_prefill_rows_per_chunk(int64_t W, int64_t budget_bytes) {
+  if (W < 1) return 0;
+  return prefill_rows_per_chunk(W, budget_bytes);
+}
+
+int64_t idx_prefill_scratch_bytes(int32_t T, int64_t W, int64_t budget_bytes) {
+  if (T < 1 || W < 1) return 0;
+  return 4 * W * prefill_chunk_rows(T, W, budget_bytes);
+}
+
+int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes) {
+  if (T < 1 || W < 1) return 0;
+  return idx_schedule_ints(prefill_ctas(prefill_chunk_rows(T, W, budget_bytes)));
+}
+
+idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
+                                    const int32_t *block_table, const int32_t *visible_end,
+                                    int32_t T, int64_t W, int64_t budget_bytes, int32_t k,
+                                    float *logits_scratch, int64_t scratch_bytes,
+                                    int32_t *cta_scratch, int64_t cta_scratch_ints,
+                                    int32_t *out_idx, void *stream) {
+  idx_status st = check_query(q);
+  if (st != IDX_OK) return st;
+  if ((st = check_cache(kv, q->dtype)) != IDX_OK) return st;
+  if (!block_table || !visible_end || !logits_scratch || !cta_scratch || !out_idx)
+    return fail(IDX_ERR_INVALID, "null block_table, visible_end, scratch or out_idx");
+  if (T < 1) return fail(IDX_ERR_INVALID, "T must be >= 1");
+  if (W < 1) return fail(IDX_ERR_INVALID, "W must be >= 1");
+  if (W > idx::kTopkMaxW)
+    return fail(IDX_ERR_UNSUPPORTED, "W = %lld above the %d-wide in-register top-k", (long long)W,
+                idx::kTopkMaxW);
+  if (k < 1) return fail(IDX_ERR_INVALID, "k = %d must be >= 1", k);
+  if (budget_bytes < 1) return fail(IDX_ERR_INVALID, "budget_bytes must be >= 1");
+  const int64_t rows = prefill_chunk_rows(T, W, budget_bytes);
+  if (scratch_bytes < 4 * W * rows)
+    return fail(IDX_ERR_WORKSPACE, "logits scratch %lld B < %lld B", (long long)scratch_bytes,
+                (long long)(4 * W * rows));
+  const int32_t n_ctas = prefill_ctas(rows);
+  if (cta_scratch_ints < idx_schedule_ints(n_ctas))
+    return fail(IDX_ERR_WORKSPACE, "schedule scratch %lld ints < %lld", (long long)cta_scratch_ints,
+                (long long)idx_schedule_ints(n_ctas));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  idx::LogitsArgs la = logits_args(q, kv);
+  la.block_tables = block_table;
+  la.bt_stride = 0;
+  la.bt_cols = (W + kv->page_size - 1) / kv->page_size;
+  la.lens = visible_end;
+  la.next_n = 1;
+  la.cta_info = cta_scratch;
+  la.n_ctas = n_ctas;
+  la.logits = logits_scratch;
+  la.W = W;
+  for (int64_t r0 = 0; r0 < T; r0 += rows) {
+    const int64_t r1 = r0 + rows < T ? r0 + rows : T;
+    const int32_t nseg =
+        (int32_t)((r1 - r0 + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg);
+    idx::ScheduleArgs sa;
+    sa.lens = visible_end;
+    sa.nseg = nseg;
+    sa.mode = idx::kSegPrefill;
+    sa.row0 = (int32_t)r0;
+    sa.row_end = (int32_t)r1;
+    sa.block_tokens = la.block_tokens;
+    sa.n_ctas = n_ctas;
+    sa.cta_info = cta_scratch;
+    hipError_t e = idx::launch_schedule(sa, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill schedule launch");
+    la.nseg = nseg;
+    la.row0 = (int32_t)r0;
+    la.row_end = (int32_t)r1;
+    e = q->dtype == IDX_FP8_E4M3 ? idx::launch_logits_fp8_prefill(la, s)
+                                 : idx::launch_logits_mxfp4_prefill(la, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill logits launch");
+    idx::TopkArgs ta;
+    ta.logits = logits_scratch;
+    ta.W = W;
+    ta.lens = visible_end + r0;
+    ta.next_n = 1;
+    ta.R = (int32_t)(r1 - r0);
+    ta.k = k;
+    ta.out_idx = out_idx + r0 * k;
+    ta.out_count = nullptr;
+    e = idx::launch_topk(ta, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill top-k launch");
+  }
+  return ok();
+}
+
+} // extern "C"

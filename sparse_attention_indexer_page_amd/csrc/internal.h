@@ -1,0 +1,88 @@
+// Internal launch interface between the C-ABI layer (idx_api.hip) and the
+// gfx950 kernels. Not installed; the public interface is include/idx.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "idx.h"
+
+namespace idx {
+
+constexpr int kHeads = 64;   // indexer heads the MFMA tiling is built for
+constexpr int kHeadDim = 128; // one 16x16x128 MFMA covers a whole head
+constexpr int kTile = 16;    // tokens per MFMA column tile
+constexpr int kMaxSegs = 16000;      // schedule segments the builder scans in LDS (64000 B)
+constexpr int kTopkMaxW = 65536;     // in-register top-k row capacity
+constexpr int kPrefillRowsPerSeg = 2; // query rows sharing one K stream in prefill
+
+// Tokens per schedule block: a block never straddles two pages.
+inline int block_tokens(int page_size) { return page_size < 64 ? page_size : 64; }
+
+enum SegMode : int {
+  kSegDecode = 0,  // segment = sequence; length = context_lens[s]
+  kSegPrefill = 1, // segment = kPrefillRowsPerSeg consecutive query rows;
+                   // length = max visible_end over those rows
+};
+
+struct ScheduleArgs {
+  const int32_t *lens; // decode: context_lens [nseg]; prefill: visible_end [T]
+  int32_t nseg;
+  int32_t mode;       // SegMode
+  int32_t row0;       // prefill: first query row of the chunk
+  int32_t row_end;    // prefill: one past the last query row of the chunk
+  int32_t block_tokens;
+  int32_t n_ctas;
+  int32_t *cta_info; // [n_ctas + 1][2]
+};
+
+struct LogitsArgs {
+  // query side
+  const uint8_t *q;       // FP8 [R][64][128] / MXFP4 [R][64][64]
+  const uint8_t *q_scale; // FP8 fp32 [R] or null / MXFP4 e8m0 [R][64][4]
+  const float *weights;   // [R][64]
+  // K cache
+  const uint8_t *kdata;
+  int64_t page_stride;
+  int64_t row_stride;
+  const uint8_t *kscale;
+  int64_t scale_page_stride;
+  int64_t scale_row_stride;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t block_tokens;
+  // addressing
+  const int32_t *block_tables; // decode [B][bt_stride]; prefill one row
+  int64_t bt_stride;           // 0 in prefill (all segments share one table)
+  int64_t bt_cols;             // readable entries per block-table row
+  const int32_t *lens;         // decode context_lens [B]; prefill visible_end [T]
+  int32_t nseg;                // decode B; prefill segments of the chunk
+  int32_t next_n;              // decode rows per sequence
+  int32_t row0;                // prefill: first row of the chunk
+  int32_t row_end;             // prefill: end row of the chunk
+  const int32_t *cta_info;
+  int32_t n_ctas;
+  // output
+  float *logits; // decode [B*next_n][W]; prefill [row_end-row0][W]
+  int64_t W;
+};
+
+struct TopkArgs {
+  const float *logits;
+  int64_t W;
+  const int32_t *lens; // decode: context_lens [B]; rows: per-row lengths [R]
+  int32_t next_n;      // rows per length entry (1 for per-row lengths)
+  int32_t R;           // rows
+  int32_t k;
+  int32_t *out_idx;   // [R][k]
+  int32_t *out_count; // [R] or null
+};
+
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+hipError_t launch_logits_fp8_decode(const LogitsArgs &a, hipStream_t s);
+hipError_t launch_logits_mxfp4_decode(const LogitsArgs &a, hipStream_t s);
+hipError_t launch_logits_fp8_prefill(const LogitsArgs &a, hipStream_t s);
+hipError_t launch_logits_mxfp4_prefill(const LogitsArgs &a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+} // namespace idx

@@ -1,0 +1,123 @@
+// Work split of the paged scoring kernel, built on the device in one launch.
+//
+// ROCm/ATOM PR #1709 ("Add fp4 indexer fo dsv4"), commit on
+// compute_varctx_schedule: building the decode schedule with many small
+// launches plus an allocation and a copy cost ~300 us per step; one kernel
+// writing straight into the fixed-address buffer a captured graph reads cut
+// it to ~40 us. This builder is that single launch: it reads the current
+// lengths on the device (so a graph replay after an in-place length update
+// sees the new lengths) and writes every work group's start coordinate.
+//
+// A segment (a sequence in decode, a pair of query rows in prefill) of length
+// L owns ceil(L / BK) blocks of BK = min(page_size, 64) tokens; BK divides the
+// page size, so a block never straddles two physical pages (vllm-project/
+// DeepGEMM PR #14: BLOCK_KV = min(PAGE_KV, 64)). Blocks of all segments, in
+// order, form one list that is cut into n_ctas contiguous ranges whose sizes
+// differ by at most one block. Entry c of the buffer is (segment, block) of
+// range c's first block; entry n_ctas is (nseg, 0).
+#include "internal.h"
+
+namespace idx {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline int32_t segment_length(const ScheduleArgs &a, int s) {
+  if (a.mode == kSegDecode) {
+    int32_t v = a.lens[s];
+    return v > 0 ? v : 0;
+  }
+  int32_t m = 0;
+  const int r0 = a.row0 + s * kPrefillRowsPerSeg;
+#pragma unroll
+  for (int i = 0; i < kPrefillRowsPerSeg; ++i) {
+    const int r = r0 + i;
+    if (r < a.row_end) {
+      const int32_t v = a.lens[r];
+      m = v > m ? v : m;
+    }
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
+  // prefix[s] = blocks of segments [0, s)
+  extern __shared__ int32_t prefix[];
+  __shared__ int32_t wave_tot[kWaves];
+  __shared__ int32_t carry;
+  __shared__ int32_t total;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+
+  for (int base = 0; base < a.nseg; base += kThreads) {
+    const int s = base + tid;
+    int32_t nb = 0;
+    if (s < a.nseg) {
+      const int32_t L = segment_length(a, s);
+      nb = (L + a.block_tokens - 1) / a.block_tokens;
+    }
+    int32_t incl = nb; // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+      int32_t v = lane < kWaves ? wave_tot[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kWaves; off <<= 1) {
+        const int32_t y = __shfl_up(v, off, 64);
+        if (lane >= off) v += y;
+      }
+      if (lane < kWaves) wave_tot[lane] = v; // inclusive over waves
+    }
+    __syncthreads();
+    const int32_t c0 = carry;
+    const int32_t before = c0 + (wave ? wave_tot[wave - 1] : 0) + incl - nb;
+    if (s < a.nseg) prefix[s] = before;
+    __syncthreads();
+    if (tid == 0) carry = c0 + wave_tot[kWaves - 1];
+    __syncthreads();
+  }
+  if (tid == 0) total = carry;
+  __syncthreads();
+
+  const int64_t N = total;
+  for (int c = tid; c <= a.n_ctas; c += kThreads) {
+    const int64_t start = (c == a.n_ctas) ? N : ((int64_t)c * N) / a.n_ctas;
+    int32_t seg, blk;
+    if (start >= N) {
+      seg = a.nseg;
+      blk = 0;
+    } else {
+      // last s with prefix[s] <= start; segment s then contains block `start`
+      int lo = 0, hi = a.nseg;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (prefix[mid] <= start) lo = mid;
+        else hi = mid;
+      }
+      seg = lo;
+      blk = (int32_t)(start - prefix[lo]);
+    }
+    a.cta_info[2 * c] = seg;
+    a.cta_info[2 * c + 1] = blk;
+  }
+}
+
+} // namespace
+
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
+  const size_t lds = sizeof(int32_t) * (size_t)(a.nseg > 0 ? a.nseg : 1);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+} // namespace idx

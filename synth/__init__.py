@@ -377,3 +377,28 @@ def workload(i: int, *, seed=None, canary=True, scale_down=1):
                            W=65536 // s, bt_width=256 // s if s <= 256 else 1,
                            seed=seed, canary=canary, name="w5_mxfp4_decode")
     raise ValueError("workload index must be 1..5")
+
+
+# --------------------------------------------------------- device placement
+
+def to_device(case, device="cuda"):
+    """Copy a case's arrays to device tensors (plain uploads). Returns a dict;
+    when the cache's scale lives inside its data buffer, ``kscale`` is None and
+    ``kscale_offset`` gives its byte offset from ``kdata``."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    c = case.cache
+    out = {
+        "q": t(case.q),
+        "q_scale": t(case.q_scale),
+        "w": t(case.w),
+        "kdata": t(c.data),
+        "kscale": None if c.scale_offset >= 0 else t(c.scale),
+        "kscale_offset": c.scale_offset,
+    }
+    if isinstance(case, DecodeCase):
+        out["block_tables"] = t(case.block_tables)
+        out["lens"] = t(case.lens)
+    else:
+        out["block_table"] = t(case.block_table)
+        out["visible_end"] = t(case.visible_end)
+    return out

@@ -1,0 +1,181 @@
+"""The C ABI without a GPU: the library loads, exports what include/idx.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_indexer_page_amd as idx
+from sparse_attention_indexer_page_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idx.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sparse_attention_indexer_page_amd import build
+        build.build()
+    return idx.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(idx_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_exactly_the_bound_functions():
+    assert _declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_plain_c():
+    src = '#include "idx.h"\nint main(void){ idx_query q; idx_kv_cache kv; (void)q; (void)kv; return 0; }\n'
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                          "-I", os.path.dirname(HEADER), "-x", "c", "-"],
+                         input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(binding.Query) == 40
+    assert ctypes.sizeof(binding.KVCache) == 64
+    src = ('#include "idx.h"\n#include <stddef.h>\n'
+           '_Static_assert(sizeof(idx_query) == 40, "q");\n'
+           '_Static_assert(sizeof(idx_kv_cache) == 64, "kv");\n'
+           '_Static_assert(offsetof(idx_kv_cache, scale) == 40, "kv scale");\n'
+           '_Static_assert(offsetof(idx_query, weights) == 32, "w");\n')
+    res = subprocess.run(["gcc", "-std=c11", "-fsyntax-only", "-I", os.path.dirname(HEADER),
+                          "-x", "c", "-"], input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings_and_version(lib):
+    assert lib.idx_status_string(0) == b"IDX_OK"
+    assert lib.idx_status_string(3) == b"IDX_ERR_WORKSPACE"
+    assert idx.idx_version() >= 100
+
+
+def _q(dtype=1, heads=64, dim=128, q=0x1000, qs=0x2000, w=0x3000):
+    return binding.Query(dtype, heads, dim, 0, q, qs, w)
+
+
+def _kv(dtype=1, P=64, pages=10, data=0x10000, ps=64 * 128, rs=128, scale=0x20000, sps=256, srs=4):
+    return binding.KVCache(dtype, P, pages, data, ps, rs, scale, sps, srs)
+
+
+def _logits(q, kv, bt=0x4000, bts=8, lens=0x5000, B=2, n=1, cta=0x6000, nc=4, out=0x7000, W=512):
+    return idx.load().idx_paged_mqa_logits(ctypes.byref(q), ctypes.byref(kv), bt, bts, lens, B, n,
+                                           cta, nc, out, W, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(heads=32), idx.IDX_ERR_UNSUPPORTED),
+    (dict(dim=64), idx.IDX_ERR_UNSUPPORTED),
+    (dict(dtype=7), idx.IDX_ERR_UNSUPPORTED),
+    (dict(q=0), idx.IDX_ERR_INVALID),
+    (dict(q=0x1001), idx.IDX_ERR_INVALID),
+    (dict(w=0), idx.IDX_ERR_INVALID),
+])
+def test_logits_rejects_bad_query(lib, mutate, status):
+    assert _logits(_q(**mutate), _kv()) == status
+    assert idx.idx_last_error_message() != ""
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(P=48), idx.IDX_ERR_INVALID),
+    (dict(P=128), idx.IDX_ERR_INVALID),
+    (dict(rs=136), idx.IDX_ERR_INVALID),
+    (dict(rs=112), idx.IDX_ERR_INVALID),
+    (dict(data=0), idx.IDX_ERR_INVALID),
+    (dict(scale=0x20002), idx.IDX_ERR_INVALID),
+    (dict(ps=64 * 128 - 16), idx.IDX_ERR_INVALID),
+    (dict(dtype=2), idx.IDX_ERR_UNSUPPORTED),
+    (dict(pages=0), idx.IDX_ERR_INVALID),
+])
+def test_logits_rejects_bad_cache(lib, mutate, status):
+    assert _logits(_q(), _kv(**mutate)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), idx.IDX_ERR_INVALID), (dict(n=5), idx.IDX_ERR_INVALID),
+    (dict(B=0), idx.IDX_ERR_INVALID), (dict(B=16001), idx.IDX_ERR_INVALID),
+    (dict(cta=0), idx.IDX_ERR_INVALID), (dict(nc=0), idx.IDX_ERR_INVALID),
+    (dict(W=0), idx.IDX_ERR_INVALID), (dict(bts=0), idx.IDX_ERR_INVALID),
+])
+def test_logits_rejects_bad_shapes(lib, kw, status):
+    assert _logits(_q(), _kv(), **kw) == status
+
+
+def test_mxfp4_query_needs_scales(lib):
+    assert _logits(_q(dtype=2, qs=0), _kv(dtype=2, ps=64 * 64, rs=64)) == idx.IDX_ERR_INVALID
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 1, 64, 8, 0x100), idx.IDX_ERR_INVALID),
+    ((0x100, 0, 1, 64, 8, 0x100), idx.IDX_ERR_INVALID),
+    ((0x100, 4, 1, 96, 8, 0x100), idx.IDX_ERR_INVALID),
+    ((0x100, 4, 1, 64, 0, 0x100), idx.IDX_ERR_INVALID),
+    ((0x100, 4, 9, 64, 8, 0x100), idx.IDX_ERR_INVALID),
+    ((0x100, 4, 1, 64, 8, 0), idx.IDX_ERR_INVALID),
+])
+def test_schedule_rejects_bad_arguments(lib, args, status):
+    assert lib.idx_build_schedule(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 512, 0x100, 2, 1, 16, 0x200, None, None, 0), idx.IDX_ERR_INVALID),
+    ((0x100, 512, 0x100, 2, 1, 0, 0x200, None, None, 0), idx.IDX_ERR_INVALID),
+    ((0x100, 0, 0x100, 2, 1, 16, 0x200, None, None, 0), idx.IDX_ERR_INVALID),
+    ((0x100, 65537, 0x100, 2, 1, 16, 0x200, None, None, 0), idx.IDX_ERR_UNSUPPORTED),
+])
+def test_topk_rejects_bad_arguments(lib, args, status):
+    assert lib.idx_topk(*args, None) == status
+
+
+def test_schedule_buffer_size():
+    assert idx.idx_schedule_ints(512) == 2 * 513
+    assert idx.idx_schedule_ints(0) == 0
+
+
+def test_prefill_chunk_rule_reproduces_the_pages_buffer_sizes():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "prefill_width_rule.json")))
+    T = g["rows"]
+    big = 1 << 62
+    # Without a budget limit the scratch is the whole [T, W] buffer.
+    full_model = 4 * T * g["model_max_width"]
+    right = idx.idx_prefill_scratch_bytes(T, g["right_sized_width"], big)
+    assert round(full_model / 1e9) == g["model_max_bytes_approx_gb"]
+    assert right == 4 * T * g["right_sized_width"]
+    assert round(right / 1e6) == g["right_sized_bytes_approx_mb"]
+    # The decimal 256 MB budget of the chunked-prefill workload forces two
+    # chunks: 15625 rows, then 759.
+    rows = idx.idx_prefill_rows_per_chunk(4096, 256_000_000)
+    assert rows == 15625 and -(-T // rows) == 2
+    assert idx.idx_prefill_scratch_bytes(T, 4096, 256_000_000) == 4 * 4096 * 15625
+    # One row per chunk at a budget below one row.
+    assert idx.idx_prefill_rows_per_chunk(4096, 1) == 1
+
+
+def test_prefill_rejects_small_scratch(lib):
+    q, kv = _q(), _kv()
+    rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
+                                      1 << 20, 16, 0x300, 16, 0x400, 1 << 20, 0x500, None)
+    assert rc == idx.IDX_ERR_WORKSPACE
+    rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
+                                      1 << 20, 16, 0x300, 1 << 30, 0x400, 2, 0x500, None)
+    assert rc == idx.IDX_ERR_WORKSPACE

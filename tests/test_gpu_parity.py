@@ -1,0 +1,186 @@
+"""Parity of the HIP path with the CPU oracle on small cases that span several
+tiles, blocks and pages plus ragged tails (every visible logit, every row)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import (DeviceCase, check_logits, check_topk_band, check_topk_exact, ensure_built,
+                      log, oracle_decode_rows, oracle_prefill_rows, run_decode, run_prefill)
+import sparse_attention_indexer_page_amd as idx
+
+pytestmark = pytest.mark.gpu
+
+# empty, one token, partial first page, page edges, several blocks, long tail
+LENS = [0, 1, 17, 31, 32, 33, 64, 65, 100, 257, 1000, 2100]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def _check_decode(case, logits, out, cnt, label):
+    rows = np.arange(case.R)
+    ref, E = oracle_decode_rows(case, rows)
+    lg = logits.numpy()
+    for r in rows:
+        what = "%s row %d (E=%d)" % (label, r, E[r])
+        check_logits(lg[r], ref[r], E[r], what)
+        assert np.all(np.isnan(lg[r, E[r]:])), what + ": wrote past the visible length"
+        check_topk_band(out[r].numpy(), ref[r], E[r], case.k, what)
+        assert cnt[r] == min(case.k, E[r])
+    return ref, E
+
+
+@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("next_n", [1, 2, 3])
+def test_decode_fp8(P, next_n):
+    log("decode fp8 P=%d next_n=%d" % (P, next_n))
+    case = synth.decode_case(LENS, next_n=next_n, P=P, k=64, W=2304, seed=100 + P + next_n)
+    logits, out, cnt = run_decode(DeviceCase(case))
+    _check_decode(case, logits, out, cnt, "fp8 P%d n%d" % (P, next_n))
+
+
+@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("next_n", [1, 2])
+def test_decode_mxfp4(P, next_n):
+    log("decode mxfp4 P=%d next_n=%d" % (P, next_n))
+    case = synth.decode_case(LENS, next_n=next_n, P=P, k=64, W=2304, dtype=synth.MXFP4,
+                             seed=200 + P + next_n)
+    logits, out, cnt = run_decode(DeviceCase(case))
+    _check_decode(case, logits, out, cnt, "mxfp4 P%d n%d" % (P, next_n))
+
+
+@pytest.mark.parametrize("layout,row_stride", [("row_inline", 144), ("page_block", None),
+                                               ("separate", 144)])
+def test_decode_fp8_cache_layouts_give_identical_bits(layout, row_stride):
+    log("layout %s stride %s" % (layout, row_stride))
+    base = synth.decode_case(LENS, next_n=2, P=32, k=64, W=2304, seed=300)
+    other = synth.decode_case(LENS, next_n=2, P=32, k=64, W=2304, seed=300, layout=layout,
+                              row_stride=row_stride)
+    la, oa, _ = run_decode(DeviceCase(base))
+    lb, ob, cb = run_decode(DeviceCase(other))
+    _check_decode(other, lb, ob, cb, "layout " + layout)
+    assert torch.equal(torch.nan_to_num(la, nan=7.0), torch.nan_to_num(lb, nan=7.0))
+    assert torch.equal(oa, ob)
+
+
+@pytest.mark.parametrize("n_ctas", [1, 3, 64, 4096])
+def test_schedule_split_does_not_change_results(n_ctas):
+    log("n_ctas %d" % n_ctas)
+    case = synth.decode_case(LENS, next_n=1, P=64, k=64, W=2304, seed=400)
+    dc = DeviceCase(case)
+    ref_l, ref_o, _ = run_decode(dc, n_ctas=512)
+    l, o, _ = run_decode(dc, n_ctas=n_ctas)
+    assert torch.equal(torch.nan_to_num(l, nan=7.0), torch.nan_to_num(ref_l, nan=7.0))
+    assert torch.equal(o, ref_o)
+
+
+def test_physical_page_permutation_gives_identical_bits():
+    case = synth.decode_case(LENS, next_n=1, P=32, k=64, W=2304, seed=500)
+    la, oa, _ = run_decode(DeviceCase(case))
+    c = case.cache
+    perm = np.random.default_rng(1).permutation(c.num_pages)
+    pages = c.data.reshape(c.num_pages, -1)
+    spages = c.scale.reshape(c.num_pages, -1)
+    nd, ns = np.empty_like(pages), np.empty_like(spages)
+    nd[perm], ns[perm] = pages, spages
+    c.data, c.scale = nd.reshape(-1), ns.reshape(-1)
+    used = case.block_tables != synth.BT_SENTINEL
+    case.block_tables[used] = perm[case.block_tables[used]]
+    lb, ob, _ = run_decode(DeviceCase(case))
+    assert torch.equal(torch.nan_to_num(la, nan=7.0), torch.nan_to_num(lb, nan=7.0))
+    assert torch.equal(oa, ob)
+
+
+def test_repeat_execution_is_bit_stable():
+    case = synth.decode_case(LENS, next_n=2, P=64, k=64, W=2304, seed=600)
+    dc = DeviceCase(case)
+    first = run_decode(dc)
+    for _ in range(3):
+        again = run_decode(dc)
+        assert torch.equal(torch.nan_to_num(first[0], nan=7.0), torch.nan_to_num(again[0], nan=7.0))
+        assert torch.equal(first[1], again[1])
+
+
+def test_bad_page_ids_read_zeros_instead_of_faulting():
+    """A block-table entry outside the pool reads as an all-zero key block:
+    those tokens score exactly 0 and every other logit is unchanged."""
+    case = synth.decode_case([200, 130], next_n=1, P=32, k=16, W=256, seed=700, canary=False)
+    good, _, _ = run_decode(DeviceCase(case))
+    case.block_tables[0, 2] = case.cache.num_pages + 5  # tokens 64..95 of sequence 0
+    case.block_tables[1, 1] = -3                          # tokens 32..63 of sequence 1
+    bad, _, _ = run_decode(DeviceCase(case))
+    assert torch.all(bad[0, 64:96] == 0) and torch.all(bad[1, 32:64] == 0)
+    keep0 = torch.ones(200, dtype=torch.bool)
+    keep0[64:96] = False
+    assert torch.equal(bad[0, :200][keep0], good[0, :200][keep0])
+    keep1 = torch.ones(130, dtype=torch.bool)
+    keep1[32:64] = False
+    assert torch.equal(bad[1, :130][keep1], good[1, :130][keep1])
+
+
+@pytest.mark.parametrize("W,k", [(300, 1), (300, 64), (4096, 512), (5000, 2048), (65536, 2048)])
+def test_topk_exact_on_oracle_logits(W, k):
+    """idx_topk on the oracle's fp32 logits (uploaded) equals the oracle's
+    top-k of the same values exactly, including planted ties and -0/+0."""
+    log("topk exact W=%d k=%d" % (W, k))
+    case = synth.decode_case([0, 1, min(W, 7), W // 3, W - 1, W], next_n=1, P=64, k=k, W=W,
+                             seed=800 + k, H=64)
+    rows = np.arange(case.R)
+    ref, E = oracle_decode_rows(case, rows)
+    f32 = ref.astype(np.float32)
+    f32[~np.isfinite(f32)] = 0.0
+    rng = np.random.default_rng(k)
+    for r in rows:  # plant ties, including across -0/+0
+        e = int(E[r])
+        if e > 4:
+            pick = rng.integers(0, e, size=max(e // 5, 2))
+            f32[r, pick] = f32[r, pick[0]]
+            f32[r, pick[:2]] = [0.0, -0.0]
+    dev = torch.from_numpy(f32).cuda()
+    lens = torch.from_numpy(case.lens).cuda()
+    out = torch.empty((case.R, k), dtype=torch.int32, device="cuda")
+    idx.idx_topk(dev, W, lens, case.B, 1, k, out)
+    torch.cuda.synchronize()
+    for r in rows:
+        check_topk_exact(out[r].cpu().numpy(), f32[r], int(E[r]), k, "row %d" % r)
+
+
+def test_topk_all_equal_and_two_values():
+    W, k = 3000, 100
+    rows = np.zeros((3, W), dtype=np.float32)
+    rows[1, ::2] = 1.0
+    rows[2] = -0.0
+    rows[2, 1::3] = 0.0
+    dev = torch.from_numpy(rows).cuda()
+    lens = torch.full((3,), W, dtype=torch.int32, device="cuda")
+    out = torch.empty((3, k), dtype=torch.int32, device="cuda")
+    idx.idx_topk(dev, W, lens, 3, 1, k, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(o[0], np.arange(k))
+    assert np.array_equal(o[1], np.arange(0, 2 * k, 2))
+    assert np.array_equal(o[2], np.arange(k))
+
+
+@pytest.mark.parametrize("dtype", [synth.FP8, synth.MXFP4])
+def test_prefill_small_matches_oracle_and_is_chunk_invariant(dtype):
+    log("prefill small dtype %d" % dtype)
+    T = 301
+    ve = np.minimum(2 * (np.arange(T) + 1), 600)  # ragged, several 64-token blocks
+    case = synth.prefill_case(T, 600, visible_end=ve, P=64, k=32, W=600, dtype=dtype,
+                              seed=900 + dtype)
+    dc = DeviceCase(case)
+    full_budget = 4 * case.W * case.T
+    scratch, out = run_prefill(dc, budget=full_budget)
+    rows = np.arange(case.T)
+    ref, E = oracle_prefill_rows(case, rows)
+    lg = scratch.numpy().reshape(case.T, case.W)
+    for r in rows:
+        check_logits(lg[r], ref[r], E[r], "prefill row %d" % r)
+        check_topk_band(out[r].numpy(), ref[r], E[r], case.k, "prefill row %d" % r)
+    for budget in (4 * case.W * 100, 4 * case.W * 7, 4 * case.W, 1):
+        _, o2 = run_prefill(dc, budget=budget)
+        assert torch.equal(o2, out), "budget %d changed the selection" % budget
