@@ -1,0 +1,329 @@
+"""Benchmark of the indexer hot path on one MI355X.
+
+Workload (the batched-decode configuration): 64 sequences, context lengths
+uniform in [1024, 32768], FP8 E4M3 queries [64, 64 heads, 128] with per-token
+scales, fp32 head weights, FP8 key cache with per-token fp32 scales in 64-row
+pages drawn at random from a 40000-page pool, top-2048, fixed logits width
+65536. One step = one HIP-graph replay of schedule + paged scores + top-k.
+
+Timing: K steps of back-to-back graph replays, bracketed by synchronize.
+Each step reads its keys from one of several copies of the page pool in
+rotation, so the data a step reads was last touched several steps earlier
+(more than the 256 MiB last-level cache ago): the timed region reads keys from
+HBM, not from the cache. The scoring kernel's average duration comes from a second pass of
+eager launches of the same kernel over the same pool rotation, each bracketed
+by events on its launch stream (rocprofv3's kernel trace of this command
+reports the same kernel's average for cross-checking).
+
+Also reported: the chunked-prefill workload (16384 rows over 4096 committed
+keys, causal (r+1)//4, budget 256e6 B, top-2048) as whole-call time, and the
+CPU oracle timed on a bounded sample of the decode workload.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("mqa_logits.hip", "internal.h"):
+        with open(os.path.join(ROOT, "sparse_attention_indexer_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(digest, launch_bytes_key):
+    """HBM bytes per scoring-kernel launch from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "mqa_logits_fp8_decode_batched_counters.json")
+    try:
+        with open(path) as fh:
+            prof = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if prof.get("kernel_source_digest") != digest:
+        return None
+    return prof.get(launch_bytes_key)
+
+
+def decode_bench(args, torch, idx, synth):
+    case = synth.workload(2, canary=False)
+    R, W, k, B = case.R, case.W, case.k, case.B
+    c = case.cache
+    log("workload 2: B=%d, sum(len)=%d, pool=%d pages" % (B, int(case.lens.sum()), c.num_pages))
+    dev = synth.to_device(case)
+    n_sets = max(4, args.pool_copies)
+    pools = [dev["kdata"]] + [dev["kdata"].clone() for _ in range(n_sets - 1)]
+    scales = [dev["kscale"]] + [dev["kscale"].clone() for _ in range(n_sets - 1)]
+    query = idx.make_query(case.dtype, dev["q"], dev["q_scale"], dev["w"])
+    kvs = [idx.make_kv_cache(case.dtype, c.page_size, c.num_pages, pools[i], c.page_stride,
+                             c.row_stride, scales[i], c.scale_page_stride, c.scale_row_stride)
+           for i in range(n_sets)]
+    n_ctas = args.ctas or idx.idx_recommended_ctas(R)
+    cta = torch.empty(idx.idx_schedule_ints(n_ctas), dtype=torch.int32, device="cuda")
+    logits = torch.zeros((R, W), dtype=torch.float32, device="cuda")
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(R, dtype=torch.int32, device="cuda")
+    bt_stride = case.block_tables.shape[1]
+
+    def schedule():
+        idx.idx_build_schedule(dev["lens"], B, case.next_n, c.page_size, n_ctas, cta)
+
+    def scores(kv):
+        idx.idx_paged_mqa_logits(query, kv, dev["block_tables"], bt_stride, dev["lens"], B,
+                                 case.next_n, cta, n_ctas, logits, W)
+
+    def topk():
+        idx.idx_topk(logits, W, dev["lens"], B, case.next_n, k, out, cnt)
+
+    def step(kv):
+        schedule()
+        scores(kv)
+        topk()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for kv in kvs:
+            step(kv)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    # One graph per pool copy; step j replays graph j % n_sets.
+    graphs = []
+    for kv in kvs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(kv)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for j in range(args.warmup):
+        graphs[j % n_sets].replay()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    t0 = time.perf_counter()
+    for j in range(K):
+        graphs[j % n_sets].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = (t1 - t0) * 1e3 / K
+
+    # Scoring kernel alone: eager launches on the same stream, same pools in
+    # rotation, each bracketed by events. A sleep kernel first lets the host
+    # queue ahead so no event waits on a launch that has not been submitted.
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    try:
+        torch.cuda._sleep(2_000_000)
+    except Exception:
+        torch.empty(1 << 28, dtype=torch.uint8, device="cuda").zero_()
+    for j in range(K):
+        kev[j][0].record()
+        scores(kvs[j % n_sets])
+        kev[j][1].record()
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+
+    lens = case.lens.astype(int)
+    E = [max(0, int(l) - (case.next_n - 1 - j)) for l in lens for j in range(case.next_n)]
+    tokens = sum(E)
+    row_bytes = 128 + 4  # FP8 key row + fp32 scale
+    kbytes = int(lens.sum()) * row_bytes
+    qbytes = R * (64 * 128 + 4 + 64 * 4)
+    lbytes = tokens * 4
+    launch_bytes = kbytes + qbytes + lbytes
+    achieved = launch_bytes / (kern_avg_ms * 1e-3) / 1e9
+    digest = kernel_source_digest()
+    traffic = traffic_from_profile(digest, "hbm_bytes_per_launch")
+    return {
+        "tokens": tokens,
+        "step_ms": step_ms,
+        "kern_avg_ms": kern_avg_ms,
+        "kern_min_ms": min(kern_ms),
+        "launch_bytes": launch_bytes,
+        "achieved_gbs": achieved,
+        "traffic": traffic,
+        "n_ctas": n_ctas,
+        "digest": digest,
+        "case": case,
+    }
+
+
+def prefill_bench(args, torch, idx, synth):
+    case = synth.workload(4, canary=False)
+    T, W, k = case.T, case.W, case.k
+    log("workload 4: T=%d, W=%d, budget=%d" % (T, W, case.budget_bytes))
+    dev = synth.to_device(case)
+    c = case.cache
+    query = idx.make_query(case.dtype, dev["q"], dev["q_scale"], dev["w"])
+    kv = idx.make_kv_cache(case.dtype, c.page_size, c.num_pages, dev["kdata"], c.page_stride,
+                           c.row_stride, dev["kscale"], c.scale_page_stride, c.scale_row_stride)
+    sb = idx.idx_prefill_scratch_bytes(T, W, case.budget_bytes)
+    si = idx.idx_prefill_schedule_ints(T, W, case.budget_bytes)
+    scratch = torch.empty(sb // 4, dtype=torch.float32, device="cuda")
+    cta = torch.empty(si, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, k), dtype=torch.int32, device="cuda")
+
+    def call():
+        idx.idx_prefill_chunked_topk(query, kv, dev["block_table"], dev["visible_end"], T, W,
+                                     case.budget_bytes, k, scratch, sb, cta, si, out)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    pairs = int(case.visible_end.astype(int).sum())
+    flops = 2.0 * pairs * 64 * 128
+    return {"ms_per_call": ms, "pairs": pairs, "flops": flops,
+            "tflops_whole_call": flops / (ms * 1e-3) / 1e12}
+
+
+def cpu_baseline(case, budget_s):
+    """The CPU oracle on a bounded sample of the decode workload."""
+    import numpy as np
+
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import oracle_cache
+
+    rows_all = np.arange(case.R)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(rows_all)
+    cache = oracle_cache(case)
+    done, tokens, elapsed = [], 0, 0.0
+    t0 = time.perf_counter()
+    chunk = max(oracle.threads(), 1)
+    i = 0
+    while i < len(order) and elapsed < budget_s:
+        rows = order[i:i + chunk]
+        lg, E = oracle.decode_logits(case.dtype, case.q, case.q_scale, case.w, case.H, case.D,
+                                     cache, case.block_tables, case.lens, case.next_n, rows,
+                                     case.W)
+        oracle.topk_rows_f32(lg.astype(np.float32), E, case.k)
+        tokens += int(E.sum())
+        done.extend(rows.tolist())
+        i += chunk
+        elapsed = time.perf_counter() - t0
+    return {
+        "value": tokens / elapsed,
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": "%d of the %d decode rows (%d scored tokens, logits + top-k), %.1f s" % (
+            len(done), case.R, tokens, elapsed),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ctas", type=int, default=0, help="schedule work groups (0: recommended)")
+    ap.add_argument("--pool-copies", type=int, default=4)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import sparse_attention_indexer_page_amd as idx
+    from sparse_attention_indexer_page_amd import binding, build
+
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    idx.load()
+    torch.cuda.set_device(0)
+
+    d = decode_bench(args, torch, idx, synth)
+    log("decode: step %.3f ms, scoring kernel %.3f ms avg (%.3f min), %.0f GB/s" % (
+        d["step_ms"], d["kern_avg_ms"], d["kern_min_ms"], d["achieved_gbs"]))
+    pre = None if args.no_prefill else prefill_bench(args, torch, idx, synth)
+    if pre:
+        log("prefill: %.3f ms per chunked call, %.1f TFLOP/s whole call" % (
+            pre["ms_per_call"], pre["tflops_whole_call"]))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(d["case"], args.cpu_budget_s)
+
+    value = d["tokens"] / (d["step_ms"] * 1e-3)
+    line = {
+        "metric": "indexer tokens scored/sec (decode step: schedule + paged FP8 MQA scores + top-k)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": d["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": "batched decode: 64 seqs, lens U[1024,32768], next_n 1, FP8 q/K + "
+                        "per-token fp32 scales, page 64, 40000-page pool, top-2048, "
+                        "hipGraph replay, logits [64, 65536]",
+            "global_batch": 64,
+            "seq_len": "U[1024,32768]",
+            "parallelism": "single GPU",
+            "n_ctas": d["n_ctas"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": d["achieved_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": d["achieved_gbs"] / HBM_PEAK_GBS,
+            "traffic": d["traffic"],
+            "kernel": "mqa_logits_kernel<FP8, 1 row>",
+            "kernel_avg_us": d["kern_avg_ms"] * 1e3,
+            "algorithmic_bytes_per_launch": d["launch_bytes"],
+        },
+        "cpu_baseline": cpu,
+    }
+    if pre:
+        line["prefill"] = {
+            "workload": "chunked prefill: 16384 rows over 4096 keys, causal (r+1)//4, "
+                        "budget 256e6 B (2 chunks), top-2048",
+            "ms_per_call": pre["ms_per_call"],
+            "tokens_per_s": pre["pairs"] / (pre["ms_per_call"] * 1e-3),
+            "fp8_tflops_whole_call": pre["tflops_whole_call"],
+            "fp8_mfma_frac_whole_call": pre["tflops_whole_call"] / FP8_MFMA_PEAK_TFLOPS,
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,6 +44,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_int64
+        lib.orc_threads.restype = ctypes.c_int
+        lib.orc_threads.argtypes = []
         lib.orc_dec_fp8_e4m3.restype = ctypes.c_double
         lib.orc_dec_fp8_e4m3.argtypes = [ctypes.c_uint8]
         lib.orc_dec_e2m1.restype = ctypes.c_double
@@ -74,6 +76,11 @@ def _ptr(a):
 
 def _u8(a):
     return None if a is None else np.ascontiguousarray(a).view(np.uint8)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's row loops use."""
+    return _load().orc_threads()
 
 
 def dec_fp8(code: int) -> float:

@@ -50,12 +50,26 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define ORC_FP8 1
 #define ORC_MXFP4 2
 
 #define ORC_OK 0
 #define ORC_BAD_ARG 1
 #define ORC_BAD_PAGE 2
+
+/* Threads the row loops use (1 without OpenMP). */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- decoders */
 

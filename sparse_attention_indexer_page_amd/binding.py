@@ -68,6 +68,10 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(
             "libidx.so is not built (%s); build it with "
             "sparse_attention_indexer_page_amd.build.build()" % path)
+    try:  # bind the HIP runtime torch already uses, so its streams are valid here
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     st = ctypes.c_int

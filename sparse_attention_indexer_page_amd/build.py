@@ -2,7 +2,8 @@
 
 Each source is compiled to an object under the package's ``_build/`` folder
 (in parallel), then linked into ``libidx.so`` next to this file. Packed FP32
-instructions are disabled for all device code.
+instructions are disabled for all device code, and MFMA results are placed in
+VGPRs (the fused epilogue reads every accumulator).
 """
 from __future__ import annotations
 
@@ -32,6 +33,8 @@ def hipcc() -> str:
 def _flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the epilogue reads them with no AGPR moves
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-command-line-argument"]
 
 

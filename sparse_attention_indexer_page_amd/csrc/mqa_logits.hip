@@ -23,9 +23,10 @@
 //     ragged-window refresh: a bounds-check-off buffer load faulted on stale
 //     metadata).
 //   * Epilogue in registers: ReLU, weight and head sum per lane (16 heads),
-//     then a two-step cross-lane sum over the four lane groups; the FP8
-//     per-token K scale and per-row q scale are positive, so they are applied
-//     outside the ReLU (relu(s*x) = s*relu(x) for s >= 0).
+//     then a cross-lane sum over the four lane groups done as a reduce-scatter
+//     with the gfx950 row-swap instructions; the FP8 per-token K scale and
+//     per-row q scale are positive, so they are applied outside the ReLU
+//     (relu(s*x) = s*relu(x) for s >= 0), once per token.
 //
 // Operand lane layout (identical for A and B, which is all a full-length dot
 // product needs): lane l serves row/column (l & 15); lane group g = l >> 4
@@ -62,13 +63,15 @@ __device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-__device__ inline v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
-
-__device__ inline float lane_xor_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+// max(x, 0) as a signed-integer max of the IEEE bits: non-negative floats
+// (and +0) keep their bits, every negative float (and -0) becomes +0. One
+// integer op, with none of the NaN canonicalization a float max carries.
+__device__ inline float relu(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
 }
+
+__device__ inline v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // Query-side registers of one segment.
 template <int DT, int NROW> struct QRegs {
@@ -152,132 +155,274 @@ __device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows
   return L;
 }
 
-template <int DT, int NROW, bool PREFILL>
-__global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
+// Length of segment s (the longest visible length among its rows).
+template <int NROW, bool PREFILL>
+__device__ inline int32_t segment_length(const LogitsArgs &a, int s) {
+  if (!PREFILL) {
+    const int32_t v = a.lens[s];
+    return v > 0 ? v : 0;
+  }
+  int32_t L = 0;
+#pragma unroll
+  for (int i = 0; i < NROW; ++i) {
+    const int r = a.row0 + s * NROW + i;
+    if (r < a.row_end) {
+      const int32_t e = a.lens[r];
+      L = e > L ? e : L;
+    }
+  }
+  return L;
+}
+
+// Position of a wave in its work group's range of (segment, block) items.
+struct Walk {
+  int s, blk; // current item
+  int se, be; // first item past the range
+  int nb;     // blocks of segment s
+};
+
+__device__ inline bool in_range(const LogitsArgs &a, const Walk &w) {
+  return w.s < a.nseg && (w.s < w.se || (w.s == w.se && w.blk < w.be));
+}
+
+// Moves to the first block of the next segment that has blocks.
+template <int NROW, bool PREFILL>
+__device__ inline bool next_segment(const LogitsArgs &a, Walk &w) {
+  w.blk = 0;
+  while (true) {
+    ++w.s;
+    if (!in_range(a, w)) return false;
+    w.nb = (segment_length<NROW, PREFILL>(a, w.s) + a.block_tokens - 1) / a.block_tokens;
+    if (w.nb > 0) return true;
+  }
+}
+
+template <int NROW, bool PREFILL>
+__device__ inline bool advance(const LogitsArgs &a, Walk &w) {
+  if (++w.blk < w.nb) return in_range(a, w);
+  return next_segment<NROW, PREFILL>(a, w);
+}
+
+// K operands of one block: TPB tiles of 16 tokens of one page.
+template <int TPB> struct KBlock {
+  v8i kb[TPB];
+  uint32_t ks[TPB]; // MXFP4: E8M0 scale of the lane's block, tile t (byte 0)
+  uint32_t ksr;     // FP8: fp32 scale bits of the token this lane stores
+  int t0;           // first token of the block
+};
+
+// A window of 64 consecutive block-table entries of one segment, one per lane,
+// so consecutive blocks find their page with a register read instead of a
+// memory round trip on the load's critical path.
+struct BtWindow {
+  int32_t v;  // entry win0 + lane of segment s's row (-1 past the row)
+  int s = -1; // segment of the window
+  int win0 = 0;
+};
+
+__device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp, BtWindow &bw) {
+  if (s != bw.s || lp < bw.win0 || lp >= bw.win0 + 64) {
+    const int lane = threadIdx.x & 63;
+    const int e = lp + lane;
+    bw.v = e < a.bt_cols ? a.block_tables[(int64_t)s * a.bt_stride + e] : -1;
+    bw.s = s;
+    bw.win0 = lp;
+  }
+  return lp < a.bt_cols ? (int64_t)__builtin_amdgcn_readlane(bw.v, lp - bw.win0) : -1;
+}
+
+// Issues the loads of block w.blk of segment w.s. Every tile is loaded, also
+// past the segment's end: those rows are inside the page (or read as zeros
+// through the buffer bound) and are never stored, and unconditional loads keep
+// the wait counts exact so the next block stays in flight during compute.
+template <int DT, int TPB>
+__device__ inline void issue_block(const LogitsArgs &a, const Walk &w, BtWindow &bw,
+                                   KBlock<TPB> &kb) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int col = lane & 15;
-  const int c = blockIdx.x;
-
-  int s = a.cta_info[2 * c];
-  int blk = a.cta_info[2 * c + 1];
-  s = s > 0 ? s : 0; // a buffer never written by the builder must not index backwards
-  blk = blk > 0 ? blk : 0;
-  const int se = a.cta_info[2 * c + 2];
-  const int be = a.cta_info[2 * c + 3];
-
   const int P = a.page_size;
-  const int BK = a.block_tokens;
+  const int t0 = w.blk * a.block_tokens;
+  const int lp = t0 / P;
+  const int slot0 = t0 - lp * P;
+  int64_t pg = page_of(a, w.s, lp, bw);
+  const bool valid = pg >= 0 && pg < a.num_pages;
+  if (!valid) pg = 0;
   const uint32_t page_bytes = (uint32_t)(P * a.row_stride);
   const uint32_t scale_bytes = (uint32_t)((P - 1) * a.scale_row_stride + 4);
-
-  QRegs<DT, NROW> Q;
-  int cur = -1;
-  int32_t L = 0, nb = 0;
-  const int32_t *bt = a.block_tables;
-
-  while (s < a.nseg && (s < se || (s == se && blk < be))) {
-    if (s != cur) {
-      int32_t rows[NROW], E[NROW], orow[NROW];
-      L = segment_rows<NROW, PREFILL>(a, s, rows, E, orow);
-      nb = (L + BK - 1) / BK;
-      if (blk >= nb) { // empty segment or a stale schedule: move on
-        ++s;
-        blk = 0;
-        continue;
-      }
-      load_query<DT, NROW>(Q, a, rows, E, orow);
-      bt = a.block_tables + (int64_t)s * a.bt_stride;
-      cur = s;
-    }
-
-    // ---- one block: up to BK/16 tiles of one page
-    const int t0 = blk * BK;
-    const int lp = t0 / P;
-    const int slot0 = t0 - lp * P;
-    int64_t pg = lp < a.bt_cols ? (int64_t)bt[lp] : -1;
-    const bool valid = pg >= 0 && pg < a.num_pages;
-    if (!valid) pg = 0;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kdata + pg * a.page_stride, valid ? page_bytes : 0u);
-    const int tend = (L - t0) < BK ? (L - t0) : BK;
-    const int ntile = (tend + kTile - 1) / kTile;
-
-    v8i kb[4];
-    uint32_t ks[4];
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kdata + pg * a.page_stride, valid ? page_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(a.kscale + pg * a.scale_page_stride, valid ? scale_bytes : 0u);
+  kb.t0 = t0;
+  if (DT == IDX_FP8_E4M3) {
+    // one scale per lane: the token this lane holds after the head-sum
+    // reduction (t0 + lane for 4-tile blocks, t0 + 16*(g/2) + col for 2-tile)
+    const uint32_t slot = (uint32_t)(slot0 + (TPB == 4 ? lane : 16 * (g >> 1) + col));
+    kb.ksr = load4(sr, slot * (uint32_t)a.scale_row_stride);
+  }
+#pragma unroll
+  for (int ti = 0; ti < TPB; ++ti) {
+    const uint32_t slot = (uint32_t)(slot0 + ti * kTile + col);
+    const uint32_t off = slot * (uint32_t)a.row_stride;
     if (DT == IDX_FP8_E4M3) {
-      const __amdgpu_buffer_rsrc_t sr =
-          make_rsrc(a.kscale + pg * a.scale_page_stride, valid ? scale_bytes : 0u);
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        if (ti < ntile) {
-          const uint32_t slot = (uint32_t)(slot0 + ti * kTile + col);
-          const uint32_t off = slot * (uint32_t)a.row_stride;
-          kb[ti] = cat(load16(kr, off + 16 * g), load16(kr, off + 64 + 16 * g));
-          ks[ti] = load4(sr, slot * (uint32_t)a.scale_row_stride);
-        }
-      }
+      kb.kb[ti] = cat(load16(kr, off + 16 * g), load16(kr, off + 64 + 16 * g));
     } else {
-      const __amdgpu_buffer_rsrc_t sr =
-          make_rsrc(a.kscale + pg * a.scale_page_stride, valid ? scale_bytes : 0u);
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        if (ti < ntile) {
-          const uint32_t slot = (uint32_t)(slot0 + ti * kTile + col);
-          const v4i lo = load16(kr, slot * (uint32_t)a.row_stride + 16 * g);
-          kb[ti] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-          ks[ti] = load4(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
-        }
-      }
-    }
-
-    float outv[NROW];
-#pragma unroll
-    for (int i = 0; i < NROW; ++i) outv[i] = 0.f;
-
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      if (ti < ntile) {
-#pragma unroll
-        for (int i = 0; i < NROW; ++i) {
-          float part = 0.f;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-            if (DT == IDX_FP8_E4M3)
-              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i][m], kb[ti], acc, kFmtFp8,
-                                                                     kFmtFp8, 0, 0, 0, 0);
-            else
-              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  Q.a[i][m], kb[ti], acc, kFmtFp4, kFmtFp4, 0, Q.asc[i][m], 0, (int)ks[ti]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) part = fmaf(Q.w[i][m][j], fmaxf(acc[j], 0.f), part);
-          }
-          part = lane_xor_sum(part);
-          if (DT == IDX_FP8_E4M3) part *= __uint_as_float(ks[ti]);
-          if (g == ti) outv[i] = part;
-        }
-      }
-    }
-
-    // lane l now holds token t0 + l (tile g, column col) of every row
-    const int t = t0 + lane;
-#pragma unroll
-    for (int i = 0; i < NROW; ++i) {
-      if (Q.out_row[i] >= 0 && lane < tend && t < Q.E[i] && t < a.W)
-        a.logits[(int64_t)Q.out_row[i] * a.W + t] = outv[i];
-    }
-
-    if (++blk >= nb) {
-      ++s;
-      blk = 0;
+      const v4i lo = load16(kr, off + 16 * g);
+      kb.kb[ti] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+      kb.ks[ti] = load4(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
     }
   }
 }
 
+// MFMAs of one 16-token tile against every head tile of every row.
+template <int DT, int NROW, int TPB>
+__device__ inline void tile_mfma(const QRegs<DT, NROW> &Q, const KBlock<TPB> &kb, int ti,
+                                 v4f (&acc)[NROW][4]) {
+#pragma unroll
+  for (int i = 0; i < NROW; ++i) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      if (DT == IDX_FP8_E4M3)
+        acc[i][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i][m], kb.kb[ti], zero,
+                                                                     kFmtFp8, kFmtFp8, 0, 0, 0, 0);
+      else
+        acc[i][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            Q.a[i][m], kb.kb[ti], zero, kFmtFp4, kFmtFp4, 0, Q.asc[i][m], 0, (int)kb.ks[ti]);
+    }
+  }
+}
+
+// Sum over lane groups g = lane >> 4 of per-lane partials p[t] (one per tile),
+// scattered so that group g ends with tile g's column totals (TPB = 4), or
+// groups 2t and 2t+1 both with tile t's (TPB = 2). Uses the gfx950 row swaps
+// (v_permlane32_swap: upper 32 lanes of x <-> lower 32 of y; v_permlane16_swap:
+// odd 16-lane rows of x <-> even rows of y), so no LDS traffic.
+template <int TPB> __device__ inline float reduce_scatter(const float (&p)[TPB]);
+
+template <> __device__ inline float reduce_scatter<4>(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]),
+                                                  false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]),
+                                                  false, false);
+  // lanes 0-31 now sum tiles 0 / 1 over both halves, lanes 32-63 tiles 2 / 3
+  const float sa = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float sb = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+template <> __device__ inline float reduce_scatter<2>(const float (&p)[2]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]),
+                                                  false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Scores of one loaded block against the segment's rows, stored to logits.
+// Tile t+1's MFMAs are issued before tile t's epilogue so the matrix core and
+// the vector ALU overlap. Every tile is computed; tokens past the segment's
+// end (whose keys may be canary bytes) only reach their own columns and are
+// never stored.
+template <int DT, int NROW, int TPB>
+__device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q, int32_t L,
+                                   const KBlock<TPB> &kb) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int t0 = kb.t0;
+  float part[NROW][TPB];
+  v4f acc[2][NROW][4];
+  tile_mfma<DT, NROW, TPB>(Q, kb, 0, acc[0]);
+#pragma unroll
+  for (int ti = 0; ti < TPB; ++ti) {
+    if (ti + 1 < TPB) tile_mfma<DT, NROW, TPB>(Q, kb, ti + 1, acc[(ti + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < NROW; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = fmaf(Q.w[i][m][j], relu(acc[ti & 1][i][m][j]), s);
+      part[i][ti] = s;
+    }
+  }
+  // token held by this lane after the reduction
+  const int t = TPB == 4 ? t0 + lane : t0 + 16 * (g >> 1) + (lane & 15);
+  const bool holder = TPB == 4 || (g & 1) == 0;
+  const int tend = L - t0; // tokens of this block that the segment has
+#pragma unroll
+  for (int i = 0; i < NROW; ++i) {
+    float v = reduce_scatter<TPB>(part[i]);
+    // the FP8 key scale of this lane's token is positive, so it commutes with
+    // the ReLU and is applied once to the head sum
+    if (DT == IDX_FP8_E4M3) v *= __uint_as_float(kb.ksr);
+    if (holder && Q.out_row[i] >= 0 && t - t0 < tend && t < Q.E[i] && t < a.W)
+      a.logits[(int64_t)Q.out_row[i] * a.W + t] = v;
+  }
+}
+
+template <int DT, int NROW, bool PREFILL>
+__device__ inline int32_t enter_segment(const LogitsArgs &a, int s, QRegs<DT, NROW> &Q) {
+  int32_t rows[NROW], E[NROW], orow[NROW];
+  const int32_t L = segment_rows<NROW, PREFILL>(a, s, rows, E, orow);
+  load_query<DT, NROW>(Q, a, rows, E, orow);
+  return L;
+}
+
+// One pipeline step: `cur` holds the loaded current block; the next block's
+// loads go into `nxt` before `cur` is scored. Returns false at the end.
+template <int DT, int NROW, bool PREFILL, int TPB>
+__device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, BtWindow &bw, QRegs<DT, NROW> &Q,
+                                     int32_t &L, KBlock<TPB> &cur, KBlock<TPB> &nxt) {
+  Walk wn = w;
+  const bool more = advance<NROW, PREFILL>(a, wn);
+  if (more) issue_block<DT, TPB>(a, wn, bw, nxt);
+  score_block<DT, NROW, TPB>(a, Q, L, cur);
+  if (!more) return false;
+  if (wn.s != w.s) L = enter_segment<DT, NROW, PREFILL>(a, wn.s, Q);
+  w = wn;
+  return true;
+}
+
+template <int DT, int NROW, bool PREFILL, int TPB>
+__global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
+  const int c = blockIdx.x;
+  Walk w;
+  w.s = a.cta_info[2 * c];
+  w.blk = a.cta_info[2 * c + 1];
+  w.s = w.s > 0 ? w.s : 0; // a buffer never written by the builder must not index backwards
+  w.blk = w.blk > 0 ? w.blk : 0;
+  w.se = a.cta_info[2 * c + 2];
+  w.be = a.cta_info[2 * c + 3];
+  if (!in_range(a, w)) return;
+  w.nb = (segment_length<NROW, PREFILL>(a, w.s) + a.block_tokens - 1) / a.block_tokens;
+  if (w.blk >= w.nb && !next_segment<NROW, PREFILL>(a, w)) return; // empty or stale entry
+
+  QRegs<DT, NROW> Q;
+  int32_t L = enter_segment<DT, NROW, PREFILL>(a, w.s, Q);
+  KBlock<TPB> A, B;
+  BtWindow bw;
+  issue_block<DT, TPB>(a, w, bw, A);
+  while (pipeline_step<DT, NROW, PREFILL, TPB>(a, w, bw, Q, L, A, B) &&
+         pipeline_step<DT, NROW, PREFILL, TPB>(a, w, bw, Q, L, B, A)) {
+  }
+}
+
+template <int DT, int NROW, bool PREFILL, int TPB>
+hipError_t launch_tpb(const LogitsArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((mqa_logits_kernel<DT, NROW, PREFILL, TPB>), dim3(a.n_ctas), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// Blocks of 32 tokens (32-row pages) hold two tiles, larger blocks four.
 template <int DT, int NROW, bool PREFILL>
 hipError_t launch(const LogitsArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((mqa_logits_kernel<DT, NROW, PREFILL>), dim3(a.n_ctas), dim3(64), 0, s, a);
-  return hipGetLastError();
+  if (a.block_tokens == 32) return launch_tpb<DT, NROW, PREFILL, 2>(a, s);
+  if (a.block_tokens == 64) return launch_tpb<DT, NROW, PREFILL, 4>(a, s);
+  return hipErrorInvalidValue;
 }
 
 template <int DT> hipError_t launch_decode(const LogitsArgs &a, hipStream_t s) {

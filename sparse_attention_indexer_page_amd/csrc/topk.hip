@@ -4,24 +4,27 @@
 // largest scores among t < E_r; equal scores go to the lower index; the
 // indices are written in ascending order and the rest of the row is -1.
 //
-// One work group per row holds the whole row in registers (up to 65536
-// scores: 16 waves x 64 lanes x 64). Scores become order-preserving uint32
-// keys (-0 folded onto +0). The exact k-th largest key is found by radix
-// select: the first digit is the top 11 bits of (key - min key) over the
-// row's actual key range, so the histogram spreads over the occupied range
-// instead of piling into a handful of exponent bins; further 11-bit digits
-// refine inside the chosen bin until one key value remains or the bin fills
-// the remaining quota exactly. Histograms live in LDS. Selection then walks
-// the row in index order: wave w owns a contiguous segment, each round covers
-// 64 consecutive indices, and ballot/popcount give every selected lane its
-// output slot, so no sort is needed and ties resolve to the lower index.
+// One work group per row; the row's keys stay in registers. Scores become
+// order-preserving uint32 keys (-0 folded onto +0); the number of keys per
+// lane is a compile-time bucket chosen from the row's actual length, so every
+// loop is fully unrolled and all loads of the row are in flight at once. The
+// exact k-th largest key is found by radix select on 12/12/8-bit digits (top
+// bits first): the first digit's histogram covers every key; the keys in the
+// chosen bin (typically a few hundred) are then compacted into LDS and only
+// they are refined, until one key value remains or a bin fills the remaining
+// quota exactly. Histograms live in LDS; the bin holding the k-th key is found
+// with a block-wide scan. Selection walks the row in index order: wave w owns
+// a contiguous segment, a counting pass gives each wave its output offset, and
+// a writing pass uses ballot/popcount per 64 indices, so no sort is needed and
+// ties resolve to the lower index. When every key equal to the threshold is
+// taken (the common case) both passes reduce to one comparison per key.
 #include "internal.h"
 
 namespace idx {
 namespace {
 
-constexpr int kBins = 2048;
-constexpr int kDigitBits = 11;
+constexpr int kBins = 4096;
+constexpr int kDigitBits = 12;
 
 __device__ inline uint32_t float_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -29,27 +32,21 @@ __device__ inline uint32_t float_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
+template <typename T> __device__ inline T wave_reduce_max(T v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(v, off, 64);
+    const T o = __shfl_xor(v, off, 64);
     v = o > v ? o : v;
   }
   return v;
 }
 
-__device__ inline uint32_t wave_min_u32(uint32_t v) {
+template <typename T> __device__ inline T wave_reduce_min(T v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(v, off, 64);
+    const T o = __shfl_xor(v, off, 64);
     v = o < v ? o : v;
   }
-  return v;
-}
-
-__device__ inline int32_t wave_sum_i32(int32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
@@ -58,182 +55,279 @@ __device__ inline int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-template <int NT, int IPT>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
-  constexpr int NW = NT / 64;
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t red_u[2 * NW];
-  __shared__ int32_t red_i[2 * NW];
-  __shared__ uint32_t s_sel[4]; // bin, count above bin, count in bin
-  if (threadIdx.x < 4) s_sel[threadIdx.x] = 0;
+constexpr int kCandCap = 4096; // keys of the first pass's bin refined in LDS
 
+struct TopkShared {
+  uint32_t hist[kBins];
+  uint32_t cand[kCandCap];
+  uint32_t red[2 * 16];
+  uint32_t sel[3]; // bin, count above it, count in it
+  uint32_t ncand;
+};
+
+// Histogram of digit(key) over the keys accepted by `in`, then the bin that
+// holds the need-th largest: returns (bin, count above it, count in it).
+template <int NT, typename Visit>
+__device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit, uint32_t &bin,
+                                  int &above, int &inbin) {
+  constexpr int NW = NT / 64;
+  constexpr int BPT = kBins / NT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  __syncthreads(); // every thread is done reading red/sel/hist of the last step
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) sm.hist[tid * BPT + q] = 0;
+  __syncthreads();
+  visit([&](uint32_t d) { atomicAdd(&sm.hist[d], 1u); });
+  __syncthreads();
+  // Block-wide scan from the highest bin down: thread t owns bins
+  // [kBins-1-t*BPT, kBins-1-(t+1)*BPT).
+  const int top = kBins - 1 - tid * BPT;
+  uint32_t cnt[BPT];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    cnt[q] = sm.hist[top - q];
+    mine += cnt[q];
+  }
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sm.red[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) before += w < wave ? sm.red[w] : 0u;
+  const uint32_t excl = before + incl - mine;
+  if (excl < (uint32_t)need && excl + mine >= (uint32_t)need) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (run < (uint32_t)need && run + cnt[q] >= (uint32_t)need) {
+        sm.sel[0] = (uint32_t)(top - q);
+        sm.sel[1] = run;
+        sm.sel[2] = cnt[q];
+      }
+      run += cnt[q];
+    }
+  }
+  __syncthreads();
+  bin = sm.sel[0];
+  above = (int)sm.sel[1];
+  inbin = (int)sm.sel[2];
+}
+
+// Selects the top k of a row of E > k scores, IPT keys per lane.
+template <int NT, int IPT>
+__device__ __forceinline__ void select_row(const float *row, int E, int k, int32_t *out,
+                                           TopkShared &sm) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rounds = (E + NW * 64 - 1) / (NW * 64); // <= IPT
+  const int base = wave * rounds * 64;               // wave's first index
+
+  // ---- keys (0 past the row: every visible key is > 0x007FFFFF)
+  uint32_t key[IPT];
+  // Loads through a buffer resource bounded by the row's E scores: past the
+  // row they return 0 without a predicate; such items then get key 0.
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(row), (short)0, E * 4, 0x00020000);
+  const uint32_t voff = (uint32_t)(base + lane) * 4u;
+  const int left = E - base - lane; // item i is visible iff 64 * i < left
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, voff, 256 * i, 0);
+    key[i] = (i < rounds && 64 * i < left) ? float_key(__uint_as_float(bits)) : 0u;
+  }
+  if (tid == 0) sm.ncand = 0;
+
+  // ---- pass 1: top 12 bits of every visible key
+  uint32_t bin;
+  int above, inbin;
+  int need = k;
+  radix_pass<NT>(
+      sm, need,
+      [&](auto add) {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i)
+          if (key[i] != 0u) add(key[i] >> 20);
+      },
+      bin, above, inbin);
+  need -= above;
+  uint32_t lo = bin << 20; // every remaining candidate is in [lo, lo + 2^20)
+  uint32_t thr;            // final rule: key > thr, plus need_eq keys == thr
+  int need_eq;
+  int n_eq_total = -1; // keys == thr in the row, when known
+  if (inbin == need) {
+    thr = lo - 1u; // lo >= the visible key in the bin > 0, so no wrap
+    need_eq = 0;
+  } else if (inbin <= kCandCap) {
+    // ---- compact the bin's keys into LDS, refine them there
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const bool c = (key[i] >> 20) == bin && key[i] != 0u;
+      const uint64_t m = __ballot(c);
+      if (m) {
+        uint32_t at = 0;
+        if (lane == 0) at = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
+        at = __shfl(at, 0, 64);
+        if (c) sm.cand[at + lanes_below(m)] = key[i];
+      }
+    }
+    __syncthreads();
+    const int nc = inbin; // == sm.ncand
+    int shift = 8;
+    while (true) {
+      const uint32_t mask = shift == 8 ? 0xFFFu : 0xFFu;
+      const uint32_t hi_mask = ~((1u << (shift + (shift == 8 ? 12 : 8))) - 1u);
+      radix_pass<NT>(
+          sm, need,
+          [&](auto add) {
+            for (int c = tid; c < nc; c += NT) {
+              const uint32_t x = sm.cand[c];
+              if ((x & hi_mask) == lo) add((x >> shift) & mask);
+            }
+          },
+          bin, above, inbin);
+      need -= above;
+      lo |= bin << shift;
+      if (inbin == need) { // the whole bin fits
+        thr = lo - 1u;
+        need_eq = 0;
+        break;
+      }
+      if (shift == 0) { // a single key value: lo
+        thr = lo;
+        need_eq = need;
+        n_eq_total = inbin;
+        break;
+      }
+      shift = 0;
+    }
+  } else {
+    // ---- a crowded bin: refine over the registers (12 then 8 more bits)
+    int shift = 8;
+    while (true) {
+      const uint32_t mask = shift == 8 ? 0xFFFu : 0xFFu;
+      const uint32_t hi_mask = ~((1u << (shift + (shift == 8 ? 12 : 8))) - 1u);
+      radix_pass<NT>(
+          sm, need,
+          [&](auto add) {
+#pragma unroll
+            for (int i = 0; i < IPT; ++i)
+              if ((key[i] & hi_mask) == lo && key[i] != 0u) add((key[i] >> shift) & mask);
+          },
+          bin, above, inbin);
+      need -= above;
+      lo |= bin << shift;
+      if (inbin == need) {
+        thr = lo - 1u;
+        need_eq = 0;
+        break;
+      }
+      if (shift == 0) {
+        thr = lo;
+        need_eq = need;
+        n_eq_total = inbin;
+        break;
+      }
+      shift = 0;
+    }
+  }
+  // every key equal to thr is taken: the rule is key >= thr_ge
+  const bool all_ties = need_eq == 0 || need_eq == n_eq_total;
+  const uint32_t thr_ge = need_eq == 0 ? thr + 1u : thr;
+
+  // ---- counting pass: per wave, keys taken wholesale and keys == thr
+  uint32_t n_gt = 0, n_eq = 0;
+  if (all_ties) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) n_gt += __popcll(__ballot(key[i] >= thr_ge));
+  } else {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) { // key 0 (past the row) never reaches thr
+      n_gt += __popcll(__ballot(key[i] > thr));
+      n_eq += __popcll(__ballot(key[i] == thr));
+    }
+  }
+  __syncthreads(); // every thread is done reading red and sel
+  if (lane == 0) {
+    sm.red[wave] = n_gt;
+    sm.red[16 + wave] = n_eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    gt_before += w < wave ? (int)sm.red[w] : 0;
+    eq_before += w < wave ? (int)sm.red[16 + w] : 0;
+  }
+
+  // ---- writing pass in index order
+  if (all_ties) {
+    int pos = gt_before;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const bool sel = key[i] >= thr_ge;
+      const uint64_t msel = __ballot(sel);
+      const int p = pos + lanes_below(msel);
+      if (sel && p < k) out[p] = base + i * 64 + lane;
+      pos += (int)__popcll(msel);
+    }
+  } else {
+    int pos = gt_before + (eq_before < need_eq ? eq_before : need_eq);
+    int eq_seen = eq_before;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const bool eq = key[i] == thr;
+      const uint64_t meq = __ballot(eq);
+      const bool sel = key[i] > thr || (eq && eq_seen + lanes_below(meq) < need_eq);
+      const uint64_t msel = __ballot(sel);
+      const int p = pos + lanes_below(msel);
+      if (sel && p < k) out[p] = base + i * 64 + lane;
+      pos += (int)__popcll(msel);
+      eq_seen += (int)__popcll(meq);
+    }
+  }
+}
+
+template <int NT, int MAXIPT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
+  __shared__ TopkShared sm;
+  const int tid = threadIdx.x;
+  if (tid < 3) sm.sel[tid] = 0; // read only after barriers that follow this
   const int r = blockIdx.x;
   const int b = r / a.next_n;
   const int j = r - b * a.next_n;
-  int64_t E = (int64_t)a.lens[b] - (a.next_n - 1 - j);
-  if (E < 0) E = 0;
-  if (E > a.W) E = a.W;
+  int64_t E64 = (int64_t)a.lens[b] - (a.next_n - 1 - j);
+  if (E64 < 0) E64 = 0;
+  if (E64 > a.W) E64 = a.W;
+  const int E = (int)E64;
   const int k = a.k;
   int32_t *out = a.out_idx + (int64_t)r * k;
-  if (a.out_count && tid == 0) a.out_count[r] = (int32_t)(E < k ? E : k);
+  if (a.out_count && tid == 0) a.out_count[r] = E < k ? E : k;
 
   if (E <= k) { // everything visible is selected
     for (int i = tid; i < k; i += NT) out[i] = i < E ? i : -1;
     return;
   }
-
-  // wave segment of seg_len indices (a multiple of 64), IPT rounds at most
-  const int rounds = (int)((E + (int64_t)NW * 64 - 1) / ((int64_t)NW * 64));
-  const int seg_len = rounds * 64;
-  const int base = wave * seg_len;
   const float *row = a.logits + (int64_t)r * a.W;
-
-  uint32_t key[IPT];
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int idx = base + i * 64 + lane;
-    key[i] = 0; // 0 = not a visible index (every finite score maps above 0x007FFFFF)
-    if (i < rounds && idx < E) {
-      key[i] = float_key(row[idx]);
-      kmax = key[i] > kmax ? key[i] : kmax;
-      kmin = key[i] < kmin ? key[i] : kmin;
-    }
-  }
-  kmax = wave_max_u32(kmax);
-  kmin = wave_min_u32(kmin);
-  if (lane == 0) {
-    red_u[wave] = kmax;
-    red_u[NW + wave] = kmin;
-  }
-  __syncthreads();
-  kmax = 0;
-  kmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    kmax = red_u[w] > kmax ? red_u[w] : kmax;
-    kmin = red_u[NW + w] < kmin ? red_u[NW + w] : kmin;
-  }
-
-  // Radix select over (key - lo) within [lo, lo + 2^shift * kBins).
-  uint32_t lo = kmin;           // every candidate key is >= lo
-  uint32_t span = kmax - kmin;  // candidates lie in [lo, lo + span]
-  int32_t need = k;             // how many of the candidates to take
-  uint32_t thr = 0;             // final threshold key
-  int32_t need_eq = 0;          // how many keys == thr to take (lowest indices)
-  bool done = false;
-  while (!done) {
-    if (span == 0) { // one key value left
-      thr = lo;
-      need_eq = need;
-      break;
-    }
-    const int bits = 32 - __clz(span);
-    const int shift = bits > kDigitBits ? bits - kDigitBits : 0;
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      if (i < rounds && key[i] >= lo && key[i] - lo <= span)
-        atomicAdd(&hist[(key[i] - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    // Find bin d* (from the top) where the running count reaches `need`.
-    if (wave == 0) {
-      constexpr int PER = kBins / 64;
-      // lane owns bins kBins-1-lane*PER down to kBins-PER-lane*PER
-      const int top = kBins - 1 - lane * PER;
-      uint32_t mine = 0;
-#pragma unroll 8
-      for (int q = 0; q < PER; ++q) mine += hist[top - q];
-      // inclusive prefix over lanes (lane 0 = highest bins)
-      uint32_t incl = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      const uint32_t excl = incl - mine;
-      if (excl < (uint32_t)need && incl >= (uint32_t)need) {
-        uint32_t run = excl;
-        for (int q = 0; q < PER; ++q) {
-          const uint32_t cq = hist[top - q];
-          if (run + cq >= (uint32_t)need) {
-            s_sel[0] = (uint32_t)(top - q);
-            s_sel[1] = run;
-            s_sel[2] = cq;
-            break;
-          }
-          run += cq;
-        }
-      }
-    }
-    __syncthreads();
-    const uint32_t d = s_sel[0];
-    const int32_t above = (int32_t)s_sel[1];
-    const int32_t inbin = (int32_t)s_sel[2];
-    __syncthreads(); // s_sel and hist are rewritten by the next pass
-    need -= above;
-    const uint32_t blo = lo + (d << shift);
-    if (inbin == need) { // the whole bin fits: take every key >= blo
-      thr = blo - 1u;    // blo >= min visible key >= 0x00800000, so no wrap
-      need_eq = 0;
-      done = true;
-      break;
-    }
-    lo = blo;
-    const uint32_t width = shift >= 32 ? 0xFFFFFFFFu : ((1u << shift) - 1u);
-    span = (kmax - lo) < width ? (kmax - lo) : width;
-  }
-
-  // Index-ordered selection: key > thr always; key == thr for the first
-  // need_eq such indices.
-  int32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    if (i < rounds) {
-      const bool valid = key[i] != 0;
-      n_gt += (valid && key[i] > thr) ? 1 : 0;
-      n_eq += (valid && key[i] == thr) ? 1 : 0;
-    }
-  }
-  n_gt = wave_sum_i32(n_gt);
-  n_eq = wave_sum_i32(n_eq);
-  if (lane == 0) {
-    red_i[wave] = n_gt;
-    red_i[NW + wave] = n_eq;
-  }
-  __syncthreads();
-  int32_t gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += red_i[w];
-    eq_before += red_i[NW + w];
-  }
-  int32_t pos = gt_before + (eq_before < need_eq ? eq_before : need_eq);
-  int32_t eq_seen = eq_before;
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    if (i < rounds) {
-      const bool valid = key[i] != 0;
-      const bool gt = valid && key[i] > thr;
-      const bool eq = valid && key[i] == thr;
-      const uint64_t meq = __ballot(eq);
-      const int eq_rank = eq_seen + lanes_below(meq);
-      const bool sel = gt || (eq && eq_rank < need_eq);
-      const uint64_t msel = __ballot(sel);
-      const int p = pos + lanes_below(msel);
-      if (sel && p < k) out[p] = base + i * 64 + lane;
-      pos += __popcll(msel);
-      eq_seen += __popcll(meq);
-    }
-  }
+  // the smallest bucket of keys per lane that holds the row
+  if (E <= NT * 4) select_row<NT, 4>(row, E, k, out, sm);
+  else if (MAXIPT >= 8 && E <= NT * 8) select_row<NT, (MAXIPT >= 8 ? 8 : 4)>(row, E, k, out, sm);
+  else if (MAXIPT >= 16 && E <= NT * 16) select_row<NT, (MAXIPT >= 16 ? 16 : 4)>(row, E, k, out, sm);
+  else if (MAXIPT >= 32 && E <= NT * 32) select_row<NT, (MAXIPT >= 32 ? 32 : 4)>(row, E, k, out, sm);
+  else if (MAXIPT >= 64) select_row<NT, (MAXIPT >= 64 ? 64 : 4)>(row, E, k, out, sm);
 }
 
-template <int NT, int IPT> hipError_t launch_rows(const TopkArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((topk_kernel<NT, IPT>), dim3(a.R), dim3(NT), 0, s, a);
+template <int NT, int MAXIPT> hipError_t launch_rows(const TopkArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((topk_kernel<NT, MAXIPT>), dim3(a.R), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -241,7 +335,6 @@ template <int NT, int IPT> hipError_t launch_rows(const TopkArgs &a, hipStream_t
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.W <= 4096) return launch_rows<256, 16>(a, s);
-  if (a.W <= 16384) return launch_rows<512, 32>(a, s);
   return launch_rows<1024, 64>(a, s);
 }
 

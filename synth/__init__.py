@@ -55,7 +55,11 @@ def quantize_fp8_rows(x: np.ndarray):
     return codes, scale
 
 
-_E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+# E2M1 rounding thresholds on |x| (scaled by the block exponent) and whether
+# the comparison is strict: at a midpoint the even code wins (round half to
+# even), e.g. 0.25 -> 0 (code 0), 0.75 -> 1.0 (code 2), 5.0 -> 4.0 (code 6).
+_E2M1_THRESHOLDS = ((0.25, True), (0.75, False), (1.25, True), (1.75, False),
+                    (2.5, True), (3.5, False), (5.0, True))
 
 
 def quantize_mxfp4(x: np.ndarray):
@@ -76,14 +80,12 @@ def quantize_mxfp4(x: np.ndarray):
         e = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, 1e-38))) - 2, 0)
     e = np.clip(e, -127, 127).astype(np.int32)
     scale_bytes = (e + 127).astype(np.uint8)
-    y = blocks / np.ldexp(np.float32(1.0), e)[..., None].astype(np.float32)
+    y = blocks * np.ldexp(np.float32(1.0), -e)[..., None].astype(np.float32)
     a = np.abs(y)
-    c = np.searchsorted(_E2M1_MIDPOINTS, a, side="left").astype(np.int32)
-    tie = np.zeros_like(a, dtype=bool)
-    inner = c < len(_E2M1_MIDPOINTS)
-    tie[inner] = a[inner] == _E2M1_MIDPOINTS[c[inner]]
-    c = np.where(tie & (c % 2 == 1), c + 1, c)
-    c = np.where((y < 0) & (c > 0), c | 8, c).astype(np.uint8)
+    c = np.zeros(a.shape, dtype=np.uint8)
+    for thr, strict in _E2M1_THRESHOLDS:
+        c += (a > thr) if strict else (a >= thr)
+    c |= ((y < 0) & (c > 0)).view(np.uint8) << 3
     c = c.reshape(x.shape[:-1] + (D,))
     packed = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
     return packed, scale_bytes.reshape(x.shape[:-1] + (D // 32,))
