@@ -168,6 +168,20 @@ def decode_bench(args, torch, idx, synth):
     }
 
 
+def counter_run(args, torch, idx, synth):
+    """For rocprofv3 --pmc: a plain copy of known size (the counter's scale
+    reference), then eager scoring launches over the pool rotation."""
+    copy_bytes = 512 << 20
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    d = decode_bench(args, torch, idx, synth)
+    log("counter run: copy of %d bytes, then %d scoring launches of %d algorithmic bytes" % (
+        copy_bytes, args.steps, d["launch_bytes"]))
+
+
 def prefill_bench(args, torch, idx, synth):
     case = synth.workload(4, canary=False)
     T, W, k = case.T, case.W, case.k
@@ -250,6 +264,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="only a reference copy + scoring launches, for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -268,6 +284,9 @@ def main():
     idx.load()
     torch.cuda.set_device(0)
 
+    if args.counters:
+        counter_run(args, torch, idx, synth)
+        return
     d = decode_bench(args, torch, idx, synth)
     log("decode: step %.3f ms, scoring kernel %.3f ms avg (%.3f min), %.0f GB/s" % (
         d["step_ms"], d["kern_avg_ms"], d["kern_min_ms"], d["achieved_gbs"]))
