@@ -1,0 +1,82 @@
+// Device helpers shared by the gfx950 scoring kernels (decode and prefill).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+namespace dev {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kFmtFp8 = 0; // f8f6f4 format code: E4M3
+constexpr int kFmtFp4 = 4; // f8f6f4 format code: E2M1
+
+// Raw buffer resource word 3 for gfx9: no swizzle, no format conversion.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+__device__ inline v4i load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// max(x, 0) as a signed-integer max of the IEEE bits: non-negative floats
+// (and +0) keep their bits, every negative float (and -0) becomes +0. One
+// integer op, with none of the NaN canonicalization a float max carries.
+__device__ inline float relu(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
+// Wave-uniform read of launch metadata (lengths, block-table entries, the
+// work schedule) through the scalar cache: a constant-address-space load at a
+// uniform address becomes s_load, counted by lgkmcnt, so waiting for it never
+// waits for the wave's outstanding vector-memory loads or stores. The data
+// must not change while the kernel runs.
+template <typename T> __device__ inline T uniform_load(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)p;
+}
+
+__device__ inline v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+
+// Sum over lane groups g = lane >> 4 of per-lane partials p[t] (one per tile),
+// scattered so that group g ends with tile g's column totals (TPB = 4), or
+// groups 2t and 2t+1 both with tile t's (TPB = 2). Uses the gfx950 row swaps
+// (v_permlane32_swap: upper 32 lanes of x <-> lower 32 of y; v_permlane16_swap:
+// odd 16-lane rows of x <-> even rows of y), so no LDS traffic.
+template <int TPB> __device__ inline float reduce_scatter(const float (&p)[TPB]);
+
+template <> __device__ inline float reduce_scatter<4>(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]),
+                                                  false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]),
+                                                  false, false);
+  // lanes 0-31 now sum tiles 0 / 1 over both halves, lanes 32-63 tiles 2 / 3
+  const float sa = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float sb = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+template <> __device__ inline float reduce_scatter<2>(const float (&p)[2]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]),
+                                                  false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+} // namespace dev
+} // namespace idx

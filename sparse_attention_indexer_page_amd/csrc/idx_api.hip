@@ -113,11 +113,13 @@ int64_t prefill_chunk_rows(int32_t T, int64_t W, int64_t budget) {
   return rows < 1 ? 1 : rows;
 }
 
-// Work groups of a prefill chunk: one per pair of query rows, at most 8192.
+// Work groups of a prefill chunk: one per block of query rows, at most 512
+// (two resident 8-wave groups per CU of an MI355X; each walks an equal share
+// of the chunk's key blocks).
 int32_t prefill_ctas(int64_t chunk_rows) {
   int64_t segs = (chunk_rows + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg;
   if (segs < 1) segs = 1;
-  return (int32_t)(segs < 8192 ? segs : 8192);
+  return (int32_t)(segs < 512 ? segs : 512);
 }
 
 } // namespace
@@ -169,6 +171,7 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
   a.row0 = 0;
   a.row_end = 0;
   a.block_tokens = idx::block_tokens(page_size);
+  a.entry_cost = idx::kDecodeEntryCost;
   a.n_ctas = n_ctas;
   a.cta_info = cta_info;
   hipError_t e = idx::launch_schedule(a, static_cast<hipStream_t>(stream));
@@ -311,6 +314,7 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
     sa.row0 = (int32_t)r0;
     sa.row_end = (int32_t)r1;
     sa.block_tokens = la.block_tokens;
+    sa.entry_cost = idx::kPrefillEntryCost;
     sa.n_ctas = n_ctas;
     sa.cta_info = cta_scratch;
     hipError_t e = idx::launch_schedule(sa, s);

@@ -14,7 +14,12 @@ constexpr int kHeadDim = 128; // one 16x16x128 MFMA covers a whole head
 constexpr int kTile = 16;    // tokens per MFMA column tile
 constexpr int kMaxSegs = 16000;      // schedule segments the builder scans in LDS (64000 B)
 constexpr int kTopkMaxW = 65536;     // in-register top-k row capacity
-constexpr int kPrefillRowsPerSeg = 2; // query rows sharing one K stream in prefill
+constexpr int kPrefillRowsPerSeg = 7;  // query rows sharing one K stream in prefill
+// Work-split cost of entering a segment, in key blocks: a prefill row block
+// reloads seven query rows (about one block's scoring time); a decode
+// sequence's query load hides under the key stream.
+constexpr int kPrefillEntryCost = 1;
+constexpr int kDecodeEntryCost = 0;
 
 // Tokens per schedule block: a block never straddles two pages.
 inline int block_tokens(int page_size) { return page_size < 64 ? page_size : 64; }
@@ -32,6 +37,7 @@ struct ScheduleArgs {
   int32_t row0;       // prefill: first query row of the chunk
   int32_t row_end;    // prefill: one past the last query row of the chunk
   int32_t block_tokens;
+  int32_t entry_cost; // cost of entering a non-empty segment, in blocks
   int32_t n_ctas;
   int32_t *cta_info; // [n_ctas + 1][2]
 };

@@ -35,43 +35,14 @@
 // per row; for MXFP4 it holds bytes [16g, 16g+16) = elements [32g, 32g+32),
 // exactly one E8M0 block. Accumulator layout of the 16x16 f32 MFMA: lane l
 // holds column (l & 15), rows 4g..4g+3.
+#include "device_common.h"
 #include "internal.h"
 
 namespace idx {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+using namespace dev;
 
-constexpr int kFmtFp8 = 0; // f8f6f4 format code: E4M3
-constexpr int kFmtFp4 = 4; // f8f6f4 format code: E2M1
-
-// Raw buffer resource word 3 for gfx9: no swizzle, no format conversion.
-constexpr int kRsrcWord3 = 0x00020000;
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
-}
-
-__device__ inline v4i load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-__device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
-// max(x, 0) as a signed-integer max of the IEEE bits: non-negative floats
-// (and +0) keep their bits, every negative float (and -0) becomes +0. One
-// integer op, with none of the NaN canonicalization a float max carries.
-__device__ inline float relu(float x) {
-  const int b = __float_as_int(x);
-  return __int_as_float(b > 0 ? b : 0);
-}
-
-__device__ inline v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // Query-side registers of one segment.
 template <int DT, int NROW> struct QRegs {
@@ -293,35 +264,6 @@ __device__ inline void tile_mfma(const QRegs<DT, NROW> &Q, const KBlock<TPB> &kb
   }
 }
 
-// Sum over lane groups g = lane >> 4 of per-lane partials p[t] (one per tile),
-// scattered so that group g ends with tile g's column totals (TPB = 4), or
-// groups 2t and 2t+1 both with tile t's (TPB = 2). Uses the gfx950 row swaps
-// (v_permlane32_swap: upper 32 lanes of x <-> lower 32 of y; v_permlane16_swap:
-// odd 16-lane rows of x <-> even rows of y), so no LDS traffic.
-template <int TPB> __device__ inline float reduce_scatter(const float (&p)[TPB]);
-
-template <> __device__ inline float reduce_scatter<4>(const float (&p)[4]) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]),
-                                                  false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]),
-                                                  false, false);
-  // lanes 0-31 now sum tiles 0 / 1 over both halves, lanes 32-63 tiles 2 / 3
-  const float sa = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const float sb = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false,
-                                                  false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-template <> __device__ inline float reduce_scatter<2>(const float (&p)[2]) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]),
-                                                  false, false);
-  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false,
-                                                  false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // Scores of one loaded block against the segment's rows, stored to logits.
 // Tile t+1's MFMAs are issued before tile t's epilogue so the matrix core and
 // the vector ALU overlap. Every tile is computed; tokens past the segment's
@@ -442,12 +384,6 @@ hipError_t launch_logits_fp8_decode(const LogitsArgs &a, hipStream_t s) {
 }
 hipError_t launch_logits_mxfp4_decode(const LogitsArgs &a, hipStream_t s) {
   return launch_decode<IDX_MXFP4>(a, s);
-}
-hipError_t launch_logits_fp8_prefill(const LogitsArgs &a, hipStream_t s) {
-  return launch<IDX_FP8_E4M3, kPrefillRowsPerSeg, true>(a, s);
-}
-hipError_t launch_logits_mxfp4_prefill(const LogitsArgs &a, hipStream_t s) {
-  return launch<IDX_MXFP4, kPrefillRowsPerSeg, true>(a, s);
 }
 
 } // namespace idx

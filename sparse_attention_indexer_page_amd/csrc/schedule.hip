@@ -8,13 +8,17 @@
 // lengths on the device (so a graph replay after an in-place length update
 // sees the new lengths) and writes every work group's start coordinate.
 //
-// A segment (a sequence in decode, a pair of query rows in prefill) of length
-// L owns ceil(L / BK) blocks of BK = min(page_size, 64) tokens; BK divides the
-// page size, so a block never straddles two physical pages (vllm-project/
-// DeepGEMM PR #14: BLOCK_KV = min(PAGE_KV, 64)). Blocks of all segments, in
-// order, form one list that is cut into n_ctas contiguous ranges whose sizes
-// differ by at most one block. Entry c of the buffer is (segment, block) of
-// range c's first block; entry n_ctas is (nseg, 0).
+// A segment (a sequence in decode, a block of query rows in prefill) of
+// length L owns ceil(L / BK) blocks of BK = min(page_size, 64) tokens; BK
+// divides the page size, so a block never straddles two physical pages
+// (vllm-project/DeepGEMM PR #14: BLOCK_KV = min(PAGE_KV, 64)). Blocks of all
+// segments, in order, form one list; a non-empty segment also carries a fixed
+// entry cost (its query load) of `entry_cost` units in front of its blocks.
+// The list is cut into n_ctas contiguous ranges of equal cost (to one unit).
+// Entry c of the buffer is (segment, block) of range c's first block -- a
+// start inside a segment's entry units is that segment's block 0, so two
+// ranges may share a start and the first of them is empty; entry n_ctas is
+// (nseg, 0).
 #include "internal.h"
 
 namespace idx {
@@ -42,7 +46,7 @@ __device__ inline int32_t segment_length(const ScheduleArgs &a, int s) {
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
-  // prefix[s] = blocks of segments [0, s)
+  // prefix[s] = cost of segments [0, s)
   extern __shared__ int32_t prefix[];
   __shared__ int32_t wave_tot[kWaves];
   __shared__ int32_t carry;
@@ -60,6 +64,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     if (s < a.nseg) {
       const int32_t L = segment_length(a, s);
       nb = (L + a.block_tokens - 1) / a.block_tokens;
+      if (nb > 0) nb += a.entry_cost;
     }
     int32_t incl = nb; // inclusive scan within the wave
 #pragma unroll
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
       seg = a.nseg;
       blk = 0;
     } else {
-      // last s with prefix[s] <= start; segment s then contains block `start`
+      // last s with prefix[s] <= start; segment s then contains unit `start`
       int lo = 0, hi = a.nseg;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -105,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
         else hi = mid;
       }
       seg = lo;
-      blk = (int32_t)(start - prefix[lo]);
+      const int64_t u = start - prefix[lo] - a.entry_cost;
+      blk = u > 0 ? (int32_t)u : 0;
     }
     a.cta_info[2 * c] = seg;
     a.cta_info[2 * c + 1] = blk;
