@@ -4,7 +4,9 @@
 // largest scores among t < E_r; equal scores go to the lower index; the
 // indices are written in ascending order and the rest of the row is -1.
 //
-// One work group per row; the row's keys stay in registers. Scores become
+// Two kernels, chosen by the logits width W. Up to W = 4096 (prefill widths)
+// one wave owns a row, with no work-group barrier (see below). Wider rows
+// take one work group per row; the row's keys stay in registers. Scores become
 // order-preserving uint32 keys (-0 folded onto +0); the number of keys per
 // lane is a compile-time bucket chosen from the row's actual length, so every
 // loop is fully unrolled and all loads of the row are in flight at once. The
@@ -18,10 +20,13 @@
 // a writing pass uses ballot/popcount per 64 indices, so no sort is needed and
 // ties resolve to the lower index. When every key equal to the threshold is
 // taken (the common case) both passes reduce to one comparison per key.
+#include "device_common.h"
 #include "internal.h"
 
 namespace idx {
 namespace {
+
+using namespace dev;
 
 constexpr int kBins = 4096;
 constexpr int kDigitBits = 12;
@@ -326,6 +331,267 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   else if (MAXIPT >= 64) select_row<NT, (MAXIPT >= 64 ? 64 : 4)>(row, E, k, out, sm);
 }
 
+// ---- one wave per row, for widths up to 4096 --------------------------------
+//
+// Short rows (prefill widths) are cheap enough that work-group barriers would
+// dominate, so each wave owns a whole row: its keys (up to 64 per lane) stay in
+// registers and the radix select runs on a per-wave LDS histogram with no
+// barrier at all. The first pass bins the row by score value, linearly between
+// the row's minimum and maximum: the map is monotone (every step rounds
+// monotonically), so a higher bin holds only larger scores, and scores spread
+// over the bins far more evenly than their float bit patterns would. The
+// chosen bin's keys, between its smallest and largest key, are then either
+// ranked directly (at most 64 of them) or binned again by key bits.
+
+constexpr int kWaveBins = 1024;
+constexpr int kRowsPerGroup = 4; // waves (rows) per work group
+constexpr int kWaveCand = 64;
+
+struct WaveShared {
+  uint32_t hist[kWaveBins];
+  uint32_t cand[kWaveCand];
+};
+
+// Waits for this wave's LDS operations; a wave's LDS accesses are then
+// visible to its own later reads in every lane.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt / expcnt not waited
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Histogram of the keys accepted by `bin_of` (which returns kWaveBins for a
+// key it skips), then the bin holding the need-th largest: its index, the
+// count in higher bins and the count in it, uniform over the wave.
+template <int IPT, typename BinOf>
+__device__ __forceinline__ void wave_radix_pass(WaveShared &sm, const uint32_t (&key)[IPT], int need,
+                                                BinOf bin_of, uint32_t &bin, int &above,
+                                                int &inbin) {
+  const int lane = threadIdx.x & 63;
+  uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist);
+#pragma unroll
+  for (int q = 0; q < kWaveBins / 256; ++q) h4[q * 64 + lane] = uint4{0u, 0u, 0u, 0u};
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const uint32_t d = bin_of(key[i]);
+    if (d < (uint32_t)kWaveBins) atomicAdd(&sm.hist[d], 1u);
+  }
+  wave_lds_sync();
+  // lane l scans bins [kWaveBins - 16 (l + 1), kWaveBins - 16 l) from the top
+  const uint4 *r4 = reinterpret_cast<const uint4 *>(sm.hist + kWaveBins - 16 * (lane + 1));
+  uint32_t cnt[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = r4[q];
+    cnt[4 * q] = v.x;
+    cnt[4 * q + 1] = v.y;
+    cnt[4 * q + 2] = v.z;
+    cnt[4 * q + 3] = v.w;
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) mine += cnt[q];
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const uint32_t excl = incl - mine;
+  const bool holder = excl < (uint32_t)need && incl >= (uint32_t)need;
+  uint32_t my_bin = 0, my_above = 0, my_in = 0;
+  if (holder) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int q = 15; q >= 0; --q) { // the lane's highest bin first
+      if (run < (uint32_t)need && run + cnt[q] >= (uint32_t)need) {
+        my_bin = (uint32_t)(kWaveBins - 16 * (lane + 1) + q);
+        my_above = run;
+        my_in = cnt[q];
+      }
+      run += cnt[q];
+    }
+  }
+  // exactly one lane holds the need-th key: the counted keys number >= need
+  const int hl = (int)__builtin_ctzll(__ballot(holder));
+  bin = __builtin_amdgcn_readlane(my_bin, hl);
+  above = (int)__builtin_amdgcn_readlane(my_above, hl);
+  inbin = (int)__builtin_amdgcn_readlane(my_in, hl);
+}
+
+template <int IPT>
+__device__ __forceinline__ void select_row_wave(const float *row, int E, int k, int32_t *out,
+                                                WaveShared &sm) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(row), (short)0, E * 4, 0x00020000);
+  uint32_t key[IPT]; // item i holds index 64 i + lane; 0 past the row
+  const int left = E - lane;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)lane * 4u, 256 * i, 0);
+    key[i] = 64 * i < left ? float_key(__uint_as_float(bits)) : 0u;
+  }
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    if (key[i] != 0u) {
+      kmax = key[i] > kmax ? key[i] : kmax;
+      kmin = key[i] < kmin ? key[i] : kmin;
+    }
+  }
+  kmax = wave_reduce_max(kmax);
+  kmin = wave_reduce_min(kmin);
+
+  // The candidates are the keys in [lo, hi]; `need` of them remain to take.
+  uint32_t lo = kmin, hi = kmax;
+  int need = k, cand = E;
+  uint32_t thr;    // final rule: key > thr, plus need_eq keys == thr (lowest index first)
+  int need_eq = 0; // 0: every key >= thr + 1 is taken
+  int n_eq_total = -1;
+  bool done = false;
+
+  // ---- pass 1 by value, linear between the row's extremes (halved so the
+  // difference cannot overflow)
+  const float h0 = key_float(kmin) * 0.5f;
+  const float hr = key_float(kmax) * 0.5f - h0;
+  const float scale = (float)kWaveBins / hr;
+  if (hr > 0.f && scale < 3.0e38f) {
+    auto vbin = [&](uint32_t kk) -> uint32_t {
+      const float x = (key_float(kk) * 0.5f - h0) * scale;
+      return (uint32_t)fminf(x, (float)(kWaveBins - 1));
+    };
+    uint32_t bin;
+    int above, inbin;
+    wave_radix_pass<IPT>(
+        sm, key, need, [&](uint32_t kk) { return kk != 0u ? vbin(kk) : (uint32_t)kWaveBins; }, bin,
+        above, inbin);
+    need -= above;
+    cand = inbin;
+    uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      uint32_t kk = key[i];
+      asm volatile("" : "+v"(kk)); // recompute the bin rather than keep 64 of them live
+      if (kk != 0u && vbin(kk) == bin) {
+        bmin = kk < bmin ? kk : bmin;
+        bmax = kk > bmax ? kk : bmax;
+      }
+    }
+    lo = wave_reduce_min(bmin); // the bin's keys are exactly those in [lo, hi]
+    hi = wave_reduce_max(bmax);
+    if (inbin == need) {
+      thr = lo - 1u; // lo >= kmin > 0
+      done = true;
+    }
+  }
+  // ---- then by key bits within [lo, hi]
+  while (!done) {
+    if (lo == hi) { // a single key value
+      thr = lo;
+      need_eq = need;
+      n_eq_total = cand;
+      break;
+    }
+    if (cand <= kWaveCand) {
+      // rank the candidates directly: lane l holds candidate l
+      uint32_t at = 0;
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const bool c = key[i] >= lo && key[i] <= hi;
+        const uint64_t m = __ballot(c);
+        if (c) sm.cand[at + lanes_below(m)] = key[i];
+        at += (uint32_t)__popcll(m);
+      }
+      wave_lds_sync();
+      const uint32_t mykey = lane < cand ? sm.cand[lane] : 0u;
+      int gt = 0, eq = 0;
+      for (int j = 0; j < cand; ++j) {
+        const uint32_t x = __builtin_amdgcn_readlane(mykey, j);
+        gt += x > mykey ? 1 : 0;
+        eq += x == mykey ? 1 : 0;
+      }
+      const bool is_thr = lane < cand && gt < need && gt + eq >= need;
+      const int tl = (int)__builtin_ctzll(__ballot(is_thr));
+      thr = __builtin_amdgcn_readlane(mykey, tl);
+      n_eq_total = __builtin_amdgcn_readlane(eq, tl);
+      need_eq = need - __builtin_amdgcn_readlane(gt, tl);
+      break;
+    }
+    const uint32_t range = hi - lo;
+    const int bits = 32 - __builtin_clz(range);
+    const int shift = bits > 10 ? bits - 10 : 0;
+    uint32_t bin;
+    int above, inbin;
+    wave_radix_pass<IPT>(
+        sm, key, need,
+        [&](uint32_t kk) {
+          return kk >= lo && kk <= hi ? (kk - lo) >> shift : (uint32_t)kWaveBins;
+        },
+        bin, above, inbin);
+    need -= above;
+    cand = inbin;
+    const uint32_t nlo = lo + (bin << shift);
+    const uint32_t width = (1u << shift) - 1u;
+    hi = hi - nlo < width ? hi : nlo + width;
+    lo = nlo;
+    if (inbin == need) { // the whole bin is taken
+      thr = lo - 1u;
+      break;
+    }
+  }
+  const bool all_ties = need_eq == 0 || need_eq == n_eq_total;
+  const uint32_t thr_ge = need_eq == 0 ? thr + 1u : thr;
+
+  // ---- indices in ascending order
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    bool sel;
+    if (all_ties) {
+      sel = key[i] >= thr_ge;
+    } else {
+      const bool eq = key[i] == thr;
+      const uint64_t meq = __ballot(eq);
+      sel = key[i] > thr || (eq && eq_seen + lanes_below(meq) < need_eq);
+      eq_seen += (int)__popcll(meq);
+    }
+    const uint64_t msel = __ballot(sel);
+    const int p = pos + lanes_below(msel);
+    if (sel && p < k) out[p] = 64 * i + lane;
+    pos += (int)__popcll(msel);
+  }
+}
+
+__global__ __launch_bounds__(64 * kRowsPerGroup) void topk_wave_kernel(TopkArgs a) {
+  __shared__ WaveShared sm[kRowsPerGroup];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kRowsPerGroup + wave;
+  if (r >= a.R) return; // waves are independent: no work-group barrier below
+  const int b = r / a.next_n;
+  const int j = r - b * a.next_n;
+  int64_t E64 = (int64_t)uniform_load(a.lens + b) - (a.next_n - 1 - j);
+  if (E64 < 0) E64 = 0;
+  if (E64 > a.W) E64 = a.W;
+  const int E = (int)E64;
+  const int k = a.k;
+  int32_t *out = a.out_idx + (int64_t)r * k;
+  if (a.out_count && lane == 0) a.out_count[r] = E < k ? E : k;
+  if (E <= k) {
+    for (int i = lane; i < k; i += 64) out[i] = i < E ? i : -1;
+    return;
+  }
+  const float *row = a.logits + (int64_t)r * a.W;
+  if (E <= 1024) select_row_wave<16>(row, E, k, out, sm[wave]);
+  else if (E <= 2048) select_row_wave<32>(row, E, k, out, sm[wave]);
+  else select_row_wave<64>(row, E, k, out, sm[wave]);
+}
+
 template <int NT, int MAXIPT> hipError_t launch_rows(const TopkArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((topk_kernel<NT, MAXIPT>), dim3(a.R), dim3(NT), 0, s, a);
   return hipGetLastError();
@@ -334,7 +600,11 @@ template <int NT, int MAXIPT> hipError_t launch_rows(const TopkArgs &a, hipStrea
 } // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
-  if (a.W <= 4096) return launch_rows<256, 16>(a, s);
+  if (a.W <= 4096) {
+    const int groups = (a.R + kRowsPerGroup - 1) / kRowsPerGroup;
+    hipLaunchKernelGGL(topk_wave_kernel, dim3(groups), dim3(64 * kRowsPerGroup), 0, s, a);
+    return hipGetLastError();
+  }
   return launch_rows<1024, 64>(a, s);
 }
 

@@ -148,6 +148,46 @@ def test_topk_exact_on_oracle_logits(W, k):
         check_topk_exact(out[r].cpu().numpy(), f32[r], int(E[r]), k, "row %d" % r)
 
 
+def _adversarial_rows(W, rng):
+    """Score rows that exercise every path of the short-row selection: wide
+    and narrow ranges, a crowded bin under far outliers (several refinement
+    passes), heavy ties, and -0/+0."""
+    rows = []
+    rows.append(rng.standard_normal(W).astype(np.float32))
+    wide = (rng.choice([-1.0, 1.0], W) * 10.0 ** rng.uniform(-30, 30, W)).astype(np.float32)
+    rows.append(wide)
+    crowd = (1.0 + 1e-6 * rng.standard_normal(W)).astype(np.float32)
+    crowd[rng.integers(0, W, 5)] = [3e38, -3e38, 1e20, -1e-20, 7.0]
+    rows.append(crowd)
+    ties = rng.integers(-3, 4, W).astype(np.float32)
+    ties[ties == 0] = -0.0
+    ties[::7] = 0.0
+    rows.append(ties)
+    steps = np.repeat(rng.standard_normal(W // 100 + 1), 100)[:W].astype(np.float32)
+    rows.append(steps)
+    return rows
+
+
+@pytest.mark.parametrize("E,k", [(65, 64), (1000, 1), (1000, 999), (1500, 700), (2049, 2048),
+                                 (3000, 2048), (4096, 2048), (4096, 4095)])
+def test_topk_short_rows_exact(E, k):
+    """Widths up to 4096 take the one-wave-per-row selection: exact against
+    the oracle's top-k of the same fp32 values on adversarial rows."""
+    W = 4096
+    rng = np.random.default_rng(E * 7 + k)
+    rows = _adversarial_rows(W, rng)
+    vals = np.stack(rows)
+    dev = torch.from_numpy(vals).cuda()
+    lens = torch.full((len(rows),), E, dtype=torch.int32, device="cuda")
+    out = torch.empty((len(rows), k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(len(rows), dtype=torch.int32, device="cuda")
+    idx.idx_topk(dev, W, lens, len(rows), 1, k, out, cnt)
+    torch.cuda.synchronize()
+    assert torch.all(cnt.cpu() == min(k, E))
+    for r in range(len(rows)):
+        check_topk_exact(out[r].cpu().numpy(), vals[r], E, k, "E=%d k=%d row %d" % (E, k, r))
+
+
 def test_topk_all_equal_and_two_values():
     W, k = 3000, 100
     rows = np.zeros((3, W), dtype=np.float32)
