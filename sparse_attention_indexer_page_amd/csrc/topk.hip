@@ -37,6 +37,11 @@ __device__ inline uint32_t float_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inverse of float_key (for keys of finite scores).
+__device__ inline float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 template <typename T> __device__ inline T wave_reduce_max(T v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -62,12 +67,16 @@ __device__ inline int lanes_below(uint64_t m) {
 
 constexpr int kCandCap = 4096; // keys of the first pass's bin refined in LDS
 
+constexpr int kRankCap = 64; // candidates ranked directly by one wave
+
 struct TopkShared {
   uint32_t hist[kBins];
   uint32_t cand[kCandCap];
+  uint32_t small[kRankCap];
   uint32_t red[2 * 16];
   uint32_t sel[3]; // bin, count above it, count in it
   uint32_t ncand;
+  uint32_t nsmall;
 };
 
 // Histogram of digit(key) over the keys accepted by `in`, then the bin that
@@ -126,6 +135,29 @@ __device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit
   inbin = (int)sm.sel[2];
 }
 
+// Block-wide max and min of per-thread values (uniform result).
+template <int NT>
+__device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint32_t &mn) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  mx = wave_reduce_max(mx);
+  mn = wave_reduce_min(mn);
+  __syncthreads(); // red is free
+  if (lane == 0) {
+    sm.red[wave] = mx;
+    sm.red[16 + wave] = mn;
+  }
+  __syncthreads();
+  mx = 0u;
+  mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mx = sm.red[w] > mx ? sm.red[w] : mx;
+    mn = sm.red[16 + w] < mn ? sm.red[16 + w] : mn;
+  }
+}
+
 // Selects the top k of a row of E > k scores, IPT keys per lane.
 template <int NT, int IPT>
 __device__ __forceinline__ void select_row(const float *row, int E, int k, int32_t *out,
@@ -150,33 +182,104 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
     const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, voff, 256 * i, 0);
     key[i] = (i < rounds && 64 * i < left) ? float_key(__uint_as_float(bits)) : 0u;
   }
-  if (tid == 0) sm.ncand = 0;
-
-  // ---- pass 1: top 12 bits of every visible key
-  uint32_t bin;
-  int above, inbin;
-  int need = k;
-  radix_pass<NT>(
-      sm, need,
-      [&](auto add) {
+  if (tid == 0) {
+    sm.ncand = 0;
+    sm.nsmall = 0;
+  }
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < IPT; ++i)
-          if (key[i] != 0u) add(key[i] >> 20);
-      },
-      bin, above, inbin);
-  need -= above;
-  uint32_t lo = bin << 20; // every remaining candidate is in [lo, lo + 2^20)
-  uint32_t thr;            // final rule: key > thr, plus need_eq keys == thr
-  int need_eq;
-  int n_eq_total = -1; // keys == thr in the row, when known
-  if (inbin == need) {
-    thr = lo - 1u; // lo >= the visible key in the bin > 0, so no wrap
-    need_eq = 0;
-  } else if (inbin <= kCandCap) {
-    // ---- compact the bin's keys into LDS, refine them there
+  for (int i = 0; i < IPT; ++i) {
+    if (key[i] != 0u) {
+      kmax = key[i] > kmax ? key[i] : kmax;
+      kmin = key[i] < kmin ? key[i] : kmin;
+    }
+  }
+  block_max_min<NT>(sm, kmax, kmin);
+
+  // The candidates are the keys in [lo, hi]; `need` of them remain to take.
+  uint32_t lo = kmin, hi = kmax;
+  int need = k, cand = E;
+  uint32_t thr;    // final rule: key > thr, plus need_eq keys == thr (lowest index first)
+  int need_eq = 0; // 0: every key >= thr + 1 is taken
+  int n_eq_total = -1;
+  bool done = false;
+  bool in_lds = false; // the candidates are sm.cand[0, nc)
+  int nc = 0;
+
+  // ---- pass 1 by value, linear between the row's extremes (a monotone map:
+  // a higher bin holds only larger scores; halved so nothing overflows)
+  const float h0 = key_float(kmin) * 0.5f;
+  const float hr = key_float(kmax) * 0.5f - h0;
+  const float scale = (float)kBins / hr;
+  if (hr > 0.f && scale < 3.0e38f) {
+    auto vbin = [&](uint32_t kk) -> uint32_t {
+      const float x = (key_float(kk) * 0.5f - h0) * scale;
+      return (uint32_t)fminf(x, (float)(kBins - 1));
+    };
+    uint32_t bin;
+    int above, inbin;
+    radix_pass<NT>(
+        sm, need,
+        [&](auto add) {
+#pragma unroll
+          for (int i = 0; i < IPT; ++i)
+            if (key[i] != 0u) add(vbin(key[i]));
+        },
+        bin, above, inbin);
+    need -= above;
+    cand = inbin;
+    uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
+    if (inbin == need || inbin > kCandCap) {
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        uint32_t kk = key[i];
+        asm volatile("" : "+v"(kk)); // recompute the bin rather than keep IPT of them live
+        if (kk != 0u && vbin(kk) == bin) {
+          bmin = kk < bmin ? kk : bmin;
+          bmax = kk > bmax ? kk : bmax;
+        }
+      }
+    } else {
+      // compact the bin's keys into LDS, then take their extremes there
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        uint32_t kk = key[i];
+        asm volatile("" : "+v"(kk));
+        const bool c = kk != 0u && vbin(kk) == bin;
+        const uint64_t m = __ballot(c);
+        if (m) {
+          uint32_t at = 0;
+          if (lane == 0) at = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
+          at = __shfl(at, 0, 64);
+          if (c) sm.cand[at + lanes_below(m)] = kk;
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < inbin; c += NT) {
+        const uint32_t x = sm.cand[c];
+        bmin = x < bmin ? x : bmin;
+        bmax = x > bmax ? x : bmax;
+      }
+      in_lds = true;
+      nc = inbin;
+    }
+    block_max_min<NT>(sm, bmax, bmin);
+    lo = bmin; // the bin's keys are exactly those in [lo, hi]
+    hi = bmax;
+    if (inbin == need) {
+      thr = lo - 1u; // lo >= kmin > 0
+      done = true;
+    }
+  }
+
+  // ---- then by key bits within [lo, hi], over the candidates compacted into
+  // LDS when they fit, else over the registers
+  if (!done && !in_lds && cand > kRankCap && cand <= kCandCap) {
+    in_lds = true;
+    nc = cand;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const bool c = (key[i] >> 20) == bin && key[i] != 0u;
+      const bool c = key[i] >= lo && key[i] <= hi;
       const uint64_t m = __ballot(c);
       if (m) {
         uint32_t at = 0;
@@ -186,63 +289,97 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
       }
     }
     __syncthreads();
-    const int nc = inbin; // == sm.ncand
-    int shift = 8;
-    while (true) {
-      const uint32_t mask = shift == 8 ? 0xFFFu : 0xFFu;
-      const uint32_t hi_mask = ~((1u << (shift + (shift == 8 ? 12 : 8))) - 1u);
+  }
+  while (!done) {
+    if (lo == hi) { // a single key value
+      thr = lo;
+      need_eq = need;
+      n_eq_total = cand;
+      break;
+    }
+    if (cand <= kRankCap) {
+      // one wave ranks the candidates: compact them, lane l holds candidate l
+      auto put = [&](uint32_t x, bool c) {
+        const uint64_t m = __ballot(c);
+        if (m) {
+          uint32_t at = 0;
+          if (lane == 0) at = atomicAdd(&sm.nsmall, (uint32_t)__popcll(m));
+          at = __shfl(at, 0, 64);
+          if (c) sm.small[at + lanes_below(m)] = x;
+        }
+      };
+      const bool direct = in_lds && cand == nc; // every compacted key is a candidate
+      if (direct) {
+        // sm.cand is complete since the barrier after the compaction
+      } else if (in_lds) {
+        for (int c0 = wave * 64; c0 < nc; c0 += NT) {
+          const int c = c0 + lane;
+          const uint32_t x = c < nc ? sm.cand[c] : 0u;
+          put(x, c < nc && x >= lo && x <= hi);
+        }
+        __syncthreads();
+      } else {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) put(key[i], key[i] >= lo && key[i] <= hi);
+        __syncthreads();
+      }
+      if (wave == 0) {
+        const uint32_t *src = direct ? sm.cand : sm.small;
+        const uint32_t mykey = lane < cand ? src[lane] : 0u;
+        int gt = 0, eq = 0;
+        for (int j = 0; j < cand; ++j) {
+          const uint32_t x = __builtin_amdgcn_readlane(mykey, j);
+          gt += x > mykey ? 1 : 0;
+          eq += x == mykey ? 1 : 0;
+        }
+        const bool is_thr = lane < cand && gt < need && gt + eq >= need;
+        const int tl = (int)__builtin_ctzll(__ballot(is_thr));
+        if (lane == tl) {
+          sm.sel[0] = mykey;
+          sm.sel[1] = (uint32_t)(need - gt);
+          sm.sel[2] = (uint32_t)eq;
+        }
+      }
+      __syncthreads();
+      thr = sm.sel[0];
+      need_eq = (int)sm.sel[1];
+      n_eq_total = (int)sm.sel[2];
+      break;
+    }
+    const uint32_t range = hi - lo;
+    const int bits = 32 - __builtin_clz(range);
+    const int shift = bits > kDigitBits ? bits - kDigitBits : 0;
+    uint32_t bin;
+    int above, inbin;
+    if (in_lds) {
       radix_pass<NT>(
           sm, need,
           [&](auto add) {
             for (int c = tid; c < nc; c += NT) {
               const uint32_t x = sm.cand[c];
-              if ((x & hi_mask) == lo) add((x >> shift) & mask);
+              if (x >= lo && x <= hi) add((x - lo) >> shift);
             }
           },
           bin, above, inbin);
-      need -= above;
-      lo |= bin << shift;
-      if (inbin == need) { // the whole bin fits
-        thr = lo - 1u;
-        need_eq = 0;
-        break;
-      }
-      if (shift == 0) { // a single key value: lo
-        thr = lo;
-        need_eq = need;
-        n_eq_total = inbin;
-        break;
-      }
-      shift = 0;
-    }
-  } else {
-    // ---- a crowded bin: refine over the registers (12 then 8 more bits)
-    int shift = 8;
-    while (true) {
-      const uint32_t mask = shift == 8 ? 0xFFFu : 0xFFu;
-      const uint32_t hi_mask = ~((1u << (shift + (shift == 8 ? 12 : 8))) - 1u);
+    } else {
       radix_pass<NT>(
           sm, need,
           [&](auto add) {
 #pragma unroll
             for (int i = 0; i < IPT; ++i)
-              if ((key[i] & hi_mask) == lo && key[i] != 0u) add((key[i] >> shift) & mask);
+              if (key[i] >= lo && key[i] <= hi) add((key[i] - lo) >> shift);
           },
           bin, above, inbin);
-      need -= above;
-      lo |= bin << shift;
-      if (inbin == need) {
-        thr = lo - 1u;
-        need_eq = 0;
-        break;
-      }
-      if (shift == 0) {
-        thr = lo;
-        need_eq = need;
-        n_eq_total = inbin;
-        break;
-      }
-      shift = 0;
+    }
+    need -= above;
+    cand = inbin;
+    const uint32_t nlo = lo + (bin << shift);
+    const uint32_t width = (1u << shift) - 1u;
+    hi = hi - nlo < width ? hi : nlo + width;
+    lo = nlo;
+    if (inbin == need) { // the whole bin is taken
+      thr = lo - 1u;
+      break;
     }
   }
   // every key equal to thr is taken: the rule is key >= thr_ge
@@ -357,10 +494,6 @@ struct WaveShared {
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt / expcnt not waited
   __builtin_amdgcn_wave_barrier();
-}
-
-__device__ inline float key_float(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
 // Histogram of the keys accepted by `bin_of` (which returns kWaveBins for a
