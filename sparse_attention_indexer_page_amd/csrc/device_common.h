@@ -38,6 +38,13 @@ __device__ inline float relu(float x) {
   return __int_as_float(b > 0 ? b : 0);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of the wave are outstanding (gfx9 layout: vmcnt in bits [3:0] and [15:14];
+// expcnt (7) and lgkmcnt (15) left unwaited).
+__device__ inline constexpr int waitcnt_vm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // Wave-uniform read of launch metadata (lengths, block-table entries, the
 // work schedule) through the scalar cache: a constant-address-space load at a
 // uniform address becomes s_load, counted by lgkmcnt, so waiting for it never

@@ -76,7 +76,7 @@ __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const
     }
     float qs = 1.f;
     if (DT == IDX_FP8_E4M3 && a.q_scale != nullptr)
-      qs = reinterpret_cast<const float *>(a.q_scale)[r];
+      qs = uniform_load(reinterpret_cast<const float *>(a.q_scale) + r);
     const float *wrow = a.weights + (int64_t)r * kHeads;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -95,54 +95,36 @@ __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const
       for (int j = 0; j < 4; ++j) Q.w[i][m][j] = wv[j] * qs;
     }
   }
+  // Wait for the query loads here, once per segment: left outstanding, the
+  // compiler's wait for them at their first use would be a full vmcnt(0) in
+  // every pass of the block loop, i.e. a wait for the next block's K loads.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// Rows, visible lengths and output rows of segment s; returns its length.
-template <int NROW, bool PREFILL>
+// Rows, visible lengths and output rows of sequence s (its next_n query
+// rows; row j sees the first len - (next_n - 1 - j) keys); returns its length.
+template <int NROW>
 __device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows, int32_t *E,
                                        int32_t *out_rows) {
+  const int32_t len = uniform_load(a.lens + s);
   int32_t L = 0;
 #pragma unroll
   for (int i = 0; i < NROW; ++i) {
-    if (PREFILL) {
-      const int r = a.row0 + s * NROW + i;
-      const bool ok = r < a.row_end;
-      int32_t e = ok ? a.lens[r] : 0;
-      e = e > 0 ? e : 0;
-      rows[i] = ok ? r : -1;
-      E[i] = e;
-      out_rows[i] = ok ? r - a.row0 : -1;
-      L = e > L ? e : L;
-    } else {
-      const int r = s * a.next_n + i;
-      int32_t e = a.lens[s] - (a.next_n - 1 - i);
-      e = e > 0 ? e : 0;
-      rows[i] = r;
-      E[i] = e;
-      out_rows[i] = r;
-      L = e > L ? e : L;
-    }
+    const int r = s * a.next_n + i;
+    int32_t e = len - (a.next_n - 1 - i);
+    e = e > 0 ? e : 0;
+    rows[i] = r;
+    E[i] = e;
+    out_rows[i] = r;
+    L = e > L ? e : L;
   }
   return L;
 }
 
-// Length of segment s (the longest visible length among its rows).
-template <int NROW, bool PREFILL>
+// Length of sequence s (its last row's visible length).
 __device__ inline int32_t segment_length(const LogitsArgs &a, int s) {
-  if (!PREFILL) {
-    const int32_t v = a.lens[s];
-    return v > 0 ? v : 0;
-  }
-  int32_t L = 0;
-#pragma unroll
-  for (int i = 0; i < NROW; ++i) {
-    const int r = a.row0 + s * NROW + i;
-    if (r < a.row_end) {
-      const int32_t e = a.lens[r];
-      L = e > L ? e : L;
-    }
-  }
-  return L;
+  const int32_t v = uniform_load(a.lens + s);
+  return v > 0 ? v : 0;
 }
 
 // Position of a wave in its work group's range of (segment, block) items.
@@ -157,21 +139,19 @@ __device__ inline bool in_range(const LogitsArgs &a, const Walk &w) {
 }
 
 // Moves to the first block of the next segment that has blocks.
-template <int NROW, bool PREFILL>
 __device__ inline bool next_segment(const LogitsArgs &a, Walk &w) {
   w.blk = 0;
   while (true) {
     ++w.s;
     if (!in_range(a, w)) return false;
-    w.nb = (segment_length<NROW, PREFILL>(a, w.s) + a.block_tokens - 1) / a.block_tokens;
+    w.nb = (segment_length(a, w.s) + a.block_tokens - 1) / a.block_tokens;
     if (w.nb > 0) return true;
   }
 }
 
-template <int NROW, bool PREFILL>
 __device__ inline bool advance(const LogitsArgs &a, Walk &w) {
   if (++w.blk < w.nb) return in_range(a, w);
-  return next_segment<NROW, PREFILL>(a, w);
+  return next_segment(a, w);
 }
 
 // K operands of one block: TPB tiles of 16 tokens of one page.
@@ -182,33 +162,23 @@ template <int TPB> struct KBlock {
   int t0;           // first token of the block
 };
 
-// A window of 64 consecutive block-table entries of one segment, one per lane,
-// so consecutive blocks find their page with a register read instead of a
-// memory round trip on the load's critical path.
-struct BtWindow {
-  int32_t v;  // entry win0 + lane of segment s's row (-1 past the row)
-  int s = -1; // segment of the window
-  int win0 = 0;
-};
-
-__device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp, BtWindow &bw) {
-  if (s != bw.s || lp < bw.win0 || lp >= bw.win0 + 64) {
-    const int lane = threadIdx.x & 63;
-    const int e = lp + lane;
-    bw.v = e < a.bt_cols ? a.block_tables[(int64_t)s * a.bt_stride + e] : -1;
-    bw.s = s;
-    bw.win0 = lp;
-  }
-  return lp < a.bt_cols ? (int64_t)__builtin_amdgcn_readlane(bw.v, lp - bw.win0) : -1;
+// Physical page of logical page lp of sequence s, or -1 past the table row.
+// A scalar load: waiting for it never waits for the K loads in flight.
+__device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp) {
+  return lp < a.bt_cols ? (int64_t)uniform_load(a.block_tables + (int64_t)s * a.bt_stride + lp) : -1;
 }
 
 // Issues the loads of block w.blk of segment w.s. Every tile is loaded, also
 // past the segment's end: those rows are inside the page (or read as zeros
 // through the buffer bound) and are never stored, and unconditional loads keep
 // the wait counts exact so the next block stays in flight during compute.
+// With live == false (no next block) the same loads go through empty buffer
+// resources: they touch no memory and return zeros, and every path through
+// the block loop then has the same number of loads in flight, which keeps the
+// compiler's wait counts partial (a path without them would force it to wait
+// for every load, including the next block's, before the first MFMA).
 template <int DT, int TPB>
-__device__ inline void issue_block(const LogitsArgs &a, const Walk &w, BtWindow &bw,
-                                   KBlock<TPB> &kb) {
+__device__ inline void issue_block(const LogitsArgs &a, const Walk &w, bool live, KBlock<TPB> &kb) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int col = lane & 15;
@@ -216,7 +186,7 @@ __device__ inline void issue_block(const LogitsArgs &a, const Walk &w, BtWindow 
   const int t0 = w.blk * a.block_tokens;
   const int lp = t0 / P;
   const int slot0 = t0 - lp * P;
-  int64_t pg = page_of(a, w.s, lp, bw);
+  int64_t pg = live ? page_of(a, w.s, lp) : -1;
   const bool valid = pg >= 0 && pg < a.num_pages;
   if (!valid) pg = 0;
   const uint32_t page_bytes = (uint32_t)(P * a.row_stride);
@@ -306,73 +276,70 @@ __device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q
   }
 }
 
-template <int DT, int NROW, bool PREFILL>
+template <int DT, int NROW>
 __device__ inline int32_t enter_segment(const LogitsArgs &a, int s, QRegs<DT, NROW> &Q) {
   int32_t rows[NROW], E[NROW], orow[NROW];
-  const int32_t L = segment_rows<NROW, PREFILL>(a, s, rows, E, orow);
+  const int32_t L = segment_rows<NROW>(a, s, rows, E, orow);
   load_query<DT, NROW>(Q, a, rows, E, orow);
   return L;
 }
 
 // One pipeline step: `cur` holds the loaded current block; the next block's
 // loads go into `nxt` before `cur` is scored. Returns false at the end.
-template <int DT, int NROW, bool PREFILL, int TPB>
-__device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, BtWindow &bw, QRegs<DT, NROW> &Q,
+template <int DT, int NROW, int TPB>
+__device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, QRegs<DT, NROW> &Q,
                                      int32_t &L, KBlock<TPB> &cur, KBlock<TPB> &nxt) {
   Walk wn = w;
-  const bool more = advance<NROW, PREFILL>(a, wn);
-  if (more) issue_block<DT, TPB>(a, wn, bw, nxt);
+  const bool more = advance(a, wn);
+  issue_block<DT, TPB>(a, wn, more, nxt);
   score_block<DT, NROW, TPB>(a, Q, L, cur);
   if (!more) return false;
-  if (wn.s != w.s) L = enter_segment<DT, NROW, PREFILL>(a, wn.s, Q);
+  if (wn.s != w.s) L = enter_segment<DT, NROW>(a, wn.s, Q);
   w = wn;
   return true;
 }
 
-template <int DT, int NROW, bool PREFILL, int TPB>
+template <int DT, int NROW, int TPB>
 __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   const int c = blockIdx.x;
   Walk w;
-  w.s = a.cta_info[2 * c];
-  w.blk = a.cta_info[2 * c + 1];
+  w.s = uniform_load(a.cta_info + 2 * c);
+  w.blk = uniform_load(a.cta_info + 2 * c + 1);
   w.s = w.s > 0 ? w.s : 0; // a buffer never written by the builder must not index backwards
   w.blk = w.blk > 0 ? w.blk : 0;
-  w.se = a.cta_info[2 * c + 2];
-  w.be = a.cta_info[2 * c + 3];
+  w.se = uniform_load(a.cta_info + 2 * c + 2);
+  w.be = uniform_load(a.cta_info + 2 * c + 3);
   if (!in_range(a, w)) return;
-  w.nb = (segment_length<NROW, PREFILL>(a, w.s) + a.block_tokens - 1) / a.block_tokens;
-  if (w.blk >= w.nb && !next_segment<NROW, PREFILL>(a, w)) return; // empty or stale entry
+  w.nb = (segment_length(a, w.s) + a.block_tokens - 1) / a.block_tokens;
+  if (w.blk >= w.nb && !next_segment(a, w)) return; // empty or stale entry
 
   QRegs<DT, NROW> Q;
-  int32_t L = enter_segment<DT, NROW, PREFILL>(a, w.s, Q);
+  int32_t L = enter_segment<DT, NROW>(a, w.s, Q);
   KBlock<TPB> A, B;
-  BtWindow bw;
-  issue_block<DT, TPB>(a, w, bw, A);
-  while (pipeline_step<DT, NROW, PREFILL, TPB>(a, w, bw, Q, L, A, B) &&
-         pipeline_step<DT, NROW, PREFILL, TPB>(a, w, bw, Q, L, B, A)) {
+  issue_block<DT, TPB>(a, w, true, A);
+  while (pipeline_step<DT, NROW, TPB>(a, w, Q, L, A, B) &&
+         pipeline_step<DT, NROW, TPB>(a, w, Q, L, B, A)) {
   }
 }
 
-template <int DT, int NROW, bool PREFILL, int TPB>
-hipError_t launch_tpb(const LogitsArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((mqa_logits_kernel<DT, NROW, PREFILL, TPB>), dim3(a.n_ctas), dim3(64), 0, s, a);
+template <int DT, int NROW, int TPB> hipError_t launch_tpb(const LogitsArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((mqa_logits_kernel<DT, NROW, TPB>), dim3(a.n_ctas), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 // Blocks of 32 tokens (32-row pages) hold two tiles, larger blocks four.
-template <int DT, int NROW, bool PREFILL>
-hipError_t launch(const LogitsArgs &a, hipStream_t s) {
-  if (a.block_tokens == 32) return launch_tpb<DT, NROW, PREFILL, 2>(a, s);
-  if (a.block_tokens == 64) return launch_tpb<DT, NROW, PREFILL, 4>(a, s);
+template <int DT, int NROW> hipError_t launch(const LogitsArgs &a, hipStream_t s) {
+  if (a.block_tokens == 32) return launch_tpb<DT, NROW, 2>(a, s);
+  if (a.block_tokens == 64) return launch_tpb<DT, NROW, 4>(a, s);
   return hipErrorInvalidValue;
 }
 
 template <int DT> hipError_t launch_decode(const LogitsArgs &a, hipStream_t s) {
   switch (a.next_n) {
-  case 1: return launch<DT, 1, false>(a, s);
-  case 2: return launch<DT, 2, false>(a, s);
-  case 3: return launch<DT, 3, false>(a, s);
-  case 4: return launch<DT, 4, false>(a, s);
+  case 1: return launch<DT, 1>(a, s);
+  case 2: return launch<DT, 2>(a, s);
+  case 3: return launch<DT, 3>(a, s);
+  case 4: return launch<DT, 4>(a, s);
   default: return hipErrorInvalidValue;
   }
 }

@@ -50,11 +50,6 @@ template <int DT, int TPB> struct Stage {
   static constexpr int kLoads = kChunks + 1; // loader instructions per stage
 };
 
-__device__ inline constexpr int waitcnt_vm(int n) {
-  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) not waited
-  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-
 template <int L> __device__ inline void wait_loads_outstanding(int items) {
   // at most `items` later stages (L loads each) may still be in flight
   static_assert(kGroup == 2 && 2 * L < 64, "one immediate per possible count");
