@@ -234,14 +234,53 @@ __device__ inline void tile_mfma(const QRegs<DT, NROW> &Q, const KBlock<TPB> &kb
   }
 }
 
-// Scores of one loaded block against the segment's rows, stored to logits.
+// Logits of up to kStageTokens consecutive tokens per row (one aligned window
+// of a segment), staged in LDS and written out 16 bytes per lane: the scores
+// of one block are only 256 B per row, and a store that small between the
+// K reads costs HBM time far beyond its size.
+constexpr int kStageTokens = 256;
+template <int NROW> struct OutStage {
+  float v[NROW][kStageTokens];
+};
+struct StageState {
+  int base = -1; // first token of the window, -1 when nothing is staged
+  int lo = 0;    // staged tokens are [lo, hi)
+  int hi = 0;
+};
+
+// Writes the staged tokens [lo, min(hi, E, W)) of each row and empties the stage.
+template <int DT, int NROW>
+__device__ inline void flush_stage(const LogitsArgs &a, const QRegs<DT, NROW> &Q,
+                                   const OutStage<NROW> &st, StageState &ss) {
+  const int lane = threadIdx.x & 63;
+  const int tok = ss.base + 4 * lane; // this lane's four tokens
+  const bool vec = (a.W & 3) == 0;    // rows start 16-byte aligned
+#pragma unroll
+  for (int i = 0; i < NROW; ++i) {
+    if (Q.out_row[i] < 0) continue;
+    int hi = ss.hi < Q.E[i] ? ss.hi : Q.E[i];
+    hi = hi < a.W ? hi : (int)a.W;
+    const v4f x = *reinterpret_cast<const v4f *>(&st.v[i][4 * lane]);
+    float *row = a.logits + (int64_t)Q.out_row[i] * a.W;
+    if (vec && tok >= ss.lo && tok + 4 <= hi) {
+      *reinterpret_cast<v4f *>(row + tok) = x;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (tok + j >= ss.lo && tok + j < hi) row[tok + j] = x[j];
+    }
+  }
+  ss.base = -1;
+}
+
+// Scores of one loaded block against the segment's rows, staged for logits.
 // Tile t+1's MFMAs are issued before tile t's epilogue so the matrix core and
 // the vector ALU overlap. Every tile is computed; tokens past the segment's
 // end (whose keys may be canary bytes) only reach their own columns and are
 // never stored.
 template <int DT, int NROW, int TPB>
 __device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q, int32_t L,
-                                   const KBlock<TPB> &kb) {
+                                   const KBlock<TPB> &kb, OutStage<NROW> &st, int base) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int t0 = kb.t0;
@@ -271,8 +310,7 @@ __device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q
     // the FP8 key scale of this lane's token is positive, so it commutes with
     // the ReLU and is applied once to the head sum
     if (DT == IDX_FP8_E4M3) v *= __uint_as_float(kb.ksr);
-    if (holder && Q.out_row[i] >= 0 && t - t0 < tend && t < Q.E[i] && t < a.W)
-      a.logits[(int64_t)Q.out_row[i] * a.W + t] = v;
+    if (holder && t - t0 < tend) st.v[i][t - base] = v;
   }
 }
 
@@ -288,11 +326,21 @@ __device__ inline int32_t enter_segment(const LogitsArgs &a, int s, QRegs<DT, NR
 // loads go into `nxt` before `cur` is scored. Returns false at the end.
 template <int DT, int NROW, int TPB>
 __device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, QRegs<DT, NROW> &Q,
-                                     int32_t &L, KBlock<TPB> &cur, KBlock<TPB> &nxt) {
+                                     int32_t &L, KBlock<TPB> &cur, KBlock<TPB> &nxt,
+                                     OutStage<NROW> &st, StageState &ss) {
   Walk wn = w;
   const bool more = advance(a, wn);
   issue_block<DT, TPB>(a, wn, more, nxt);
-  score_block<DT, NROW, TPB>(a, Q, L, cur);
+  if (ss.base < 0) {
+    ss.base = cur.t0 & ~(kStageTokens - 1);
+    ss.lo = cur.t0;
+  }
+  score_block<DT, NROW, TPB>(a, Q, L, cur, st, ss.base);
+  const int have = L - cur.t0; // tokens of this block that the segment has
+  ss.hi = cur.t0 + (have < a.block_tokens ? have : a.block_tokens);
+  // the next block continues this window only within the same segment
+  if (!more || wn.s != w.s || ((wn.blk * a.block_tokens) & ~(kStageTokens - 1)) != ss.base)
+    flush_stage<DT, NROW>(a, Q, st, ss);
   if (!more) return false;
   if (wn.s != w.s) L = enter_segment<DT, NROW>(a, wn.s, Q);
   w = wn;
@@ -313,12 +361,16 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   w.nb = (segment_length(a, w.s) + a.block_tokens - 1) / a.block_tokens;
   if (w.blk >= w.nb && !next_segment(a, w)) return; // empty or stale entry
 
-  QRegs<DT, NROW> Q;
-  int32_t L = enter_segment<DT, NROW>(a, w.s, Q);
+  // the first block's K loads go out before the query's, so the two
+  // latencies overlap
   KBlock<TPB> A, B;
   issue_block<DT, TPB>(a, w, true, A);
-  while (pipeline_step<DT, NROW, TPB>(a, w, Q, L, A, B) &&
-         pipeline_step<DT, NROW, TPB>(a, w, Q, L, B, A)) {
+  QRegs<DT, NROW> Q;
+  int32_t L = enter_segment<DT, NROW>(a, w.s, Q);
+  __shared__ OutStage<NROW> st;
+  StageState ss;
+  while (pipeline_step<DT, NROW, TPB>(a, w, Q, L, A, B, st, ss) &&
+         pipeline_step<DT, NROW, TPB>(a, w, Q, L, B, A, st, ss)) {
   }
 }
 
