@@ -41,9 +41,12 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "mqa_logits_fp8_decode_batched_counters")
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
-    for f in ("mqa_logits.hip", "internal.h"):
+    for f in ("mqa_logits.hip", "device_common.h", "internal.h"):
         with open(os.path.join(ROOT, "sparse_attention_indexer_page_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -52,7 +55,7 @@ def kernel_source_digest():
 def traffic_from_profile(digest, launch_bytes_key):
     """HBM bytes per scoring-kernel launch from the committed counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "mqa_logits_fp8_decode_batched_counters.json")
+    path = COUNTER_SUMMARY + ".json"
     try:
         with open(path) as fh:
             prof = json.load(fh)
@@ -182,6 +185,86 @@ def counter_run(args, torch, idx, synth):
         copy_bytes, args.steps, d["launch_bytes"]))
 
 
+def summarize_counters(fetch_dir, write_dir):
+    """Turns the two rocprofv3 --pmc runs of `--counters` (FETCH_SIZE, then
+    WRITE_SIZE) into the HBM traffic summary the bench line reads: per-dispatch
+    KiB scaled by what the same counter reads for the reference copy."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter_collection.csv under %s" % d)
+        vals = {}
+        with open(files[0]) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (_, name), v in sorted(vals.items()):
+            out.setdefault(name, []).append(v)
+        return out
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    pick = lambda m, frag: next(v for n, v in m.items() if frag in n)
+    copy_bytes = 512 << 20
+    cf, cw = pick(fetch, "copyBuffer")[0], pick(write, "copyBuffer")[0]
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    sf, sw = pick(fetch, "mqa_logits_kernel"), pick(write, "mqa_logits_kernel")
+    kf, kw = sum(sf) / len(sf), sum(sw) / len(sw)
+    read_b, write_b = kf * 1024 * fs, kw * 1024 * ws
+    import synth
+    case = synth.workload(2, canary=False)
+    algo = int(case.lens.astype(int).sum()) * (128 + 4 + 4) + case.R * (64 * 128 + 4 + 64 * 4)
+    summary = {
+        "kernel": "mqa_logits_kernel<FP8, 1 row, 4 tiles>",
+        "workload": "batched decode: 64 seqs, lens U[1024,32768], FP8, page 64, 40000-page pool",
+        "kernel_source_digest": kernel_source_digest(),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- "
+            "python3 -u bench.py --counters --steps 8",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write> -o run -- "
+            "python3 -u bench.py --counters --steps 8",
+            "python3 bench.py --summarize-counters <fetch> <write>",
+        ],
+        "reference_copy_bytes": copy_bytes,
+        "reference_copy_fetch_kib": cf,
+        "reference_copy_write_kib": cw,
+        "fetch_scale": fs,
+        "write_scale": ws,
+        "scoring_fetch_kib_per_launch": kf,
+        "scoring_write_kib_per_launch": kw,
+        "scoring_launches": len(sf),
+        "hbm_read_bytes_per_launch": read_b,
+        "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": read_b + write_b,
+        "algorithmic_bytes_per_launch": algo,
+    }
+    with open(COUNTER_SUMMARY + ".json", "w") as fh:
+        json.dump(summary, fh, indent=1)
+    with open(COUNTER_SUMMARY + ".md", "w") as fh:
+        fh.write("# HBM traffic of the batched-decode scoring launch (rocprofv3 PMC)\n\n")
+        fh.write("Commands (repository root, one MI355X; FETCH_SIZE and WRITE_SIZE in separate "
+                 "runs):\n\n```\n%s\n```\n\n" % "\n".join(summary["commands"]))
+        fh.write("`bench.py --counters` copies a 512 MiB tensor (one `__amd_rocclr_copyBuffer` "
+                 "dispatch that must read and write 536,870,912 bytes), then launches the scoring "
+                 "kernel over the rotated page pools.\n\n")
+        fh.write("| dispatch | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) |\n|---|---|---|\n")
+        fh.write("| reference copy, 512 MiB | %s | %s |\n" % (f"{cf:,.0f}", f"{cw:,.0f}"))
+        fh.write("| scoring kernel (avg of %d) | %s | %s |\n\n" % (
+            len(sf), f"{kf:,.0f}", f"{kw:,.0f}"))
+        fh.write("Scale factors from the reference copy: reads x%.3f, writes x%.3f. Scoring launch: "
+                 "%.1f MB read + %.2f MB written = %.1f MB of HBM traffic against %.1f MB "
+                 "algorithmic (%.1f%%). Kernel source digest: `%s`.\n" % (
+                     fs, ws, read_b / 1e6, write_b / 1e6, (read_b + write_b) / 1e6, algo / 1e6,
+                     100.0 * (read_b + write_b) / algo, summary["kernel_source_digest"]))
+    log("wrote %s.{json,md}: %.1f MB per launch (%.1f MB algorithmic)" % (
+        COUNTER_SUMMARY, (read_b + write_b) / 1e6, algo / 1e6))
+
+
 def prefill_bench(args, torch, idx, synth):
     case = synth.workload(4, canary=False)
     T, W, k = case.T, case.W, case.k
@@ -266,7 +349,12 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--counters", action="store_true",
                     help="only a reference copy + scoring launches, for rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ traffic summary from two --counters PMC runs")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sequences shard across GPUs with no exchange; see the design notes)",
