@@ -66,11 +66,11 @@ def traffic_from_profile(digest, launch_bytes_key):
     return prof.get(launch_bytes_key)
 
 
-def decode_bench(args, torch, idx, synth):
-    case = synth.workload(2, canary=False)
+def decode_bench(args, torch, idx, synth, wl=2):
+    case = synth.workload(wl, canary=False)
     R, W, k, B = case.R, case.W, case.k, case.B
     c = case.cache
-    log("workload 2: B=%d, sum(len)=%d, pool=%d pages" % (B, int(case.lens.sum()), c.num_pages))
+    log("workload %d: B=%d, sum(len)=%d, pool=%d pages" % (wl, B, int(case.lens.sum()), c.num_pages))
     dev = synth.to_device(case)
     n_sets = max(4, args.pool_copies)
     pools = [dev["kdata"]] + [dev["kdata"].clone() for _ in range(n_sets - 1)]
@@ -149,9 +149,10 @@ def decode_bench(args, torch, idx, synth):
     lens = case.lens.astype(int)
     E = [max(0, int(l) - (case.next_n - 1 - j)) for l in lens for j in range(case.next_n)]
     tokens = sum(E)
-    row_bytes = 128 + 4  # FP8 key row + fp32 scale
+    fp8 = case.dtype == synth.FP8
+    row_bytes = 128 + 4 if fp8 else 64 + 4  # key row + its scale(s)
     kbytes = int(lens.sum()) * row_bytes
-    qbytes = R * (64 * 128 + 4 + 64 * 4)
+    qbytes = R * ((64 * 128 + 4) if fp8 else (64 * 64 + 64 * 4)) + R * 64 * 4
     lbytes = tokens * 4
     launch_bytes = kbytes + qbytes + lbytes
     achieved = launch_bytes / (kern_avg_ms * 1e-3) / 1e9
@@ -349,6 +350,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--counters", action="store_true",
                     help="only a reference copy + scoring launches, for rocprofv3 --pmc runs")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="also time the other decode workloads (single sequence, MTP page 32, MXFP4)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ traffic summary from two --counters PMC runs")
     args = ap.parse_args()
@@ -382,6 +385,18 @@ def main():
     if pre:
         log("prefill: %.3f ms per chunked call, %.1f TFLOP/s whole call" % (
             pre["ms_per_call"], pre["tflops_whole_call"]))
+    others = []
+    if args.all_workloads:
+        for wl in (1, 3, 5):
+            o = decode_bench(args, torch, idx, synth, wl)
+            log("workload %d: step %.3f ms, scoring kernel %.3f ms avg, %.0f GB/s (%.1f%% of peak)" % (
+                wl, o["step_ms"], o["kern_avg_ms"], o["achieved_gbs"],
+                100.0 * o["achieved_gbs"] / HBM_PEAK_GBS))
+            others.append({"workload": synth.WORKLOADS[wl], "tokens": o["tokens"],
+                           "ms_per_step": o["step_ms"], "scoring_kernel_us": o["kern_avg_ms"] * 1e3,
+                           "tokens_per_s": o["tokens"] / (o["step_ms"] * 1e-3),
+                           "achieved_gbs": o["achieved_gbs"],
+                           "hbm_frac": o["achieved_gbs"] / HBM_PEAK_GBS})
     cpu = None if args.no_cpu_baseline else cpu_baseline(d["case"], args.cpu_budget_s)
 
     value = d["tokens"] / (d["step_ms"] * 1e-3)
@@ -429,6 +444,8 @@ def main():
             "fp8_tflops_whole_call": pre["tflops_whole_call"],
             "fp8_mfma_frac_whole_call": pre["tflops_whole_call"] / FP8_MFMA_PEAK_TFLOPS,
         }
+    if others:
+        line["other_decode_workloads"] = others
     print(json.dumps(line), flush=True)
 
 

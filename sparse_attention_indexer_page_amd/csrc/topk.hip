@@ -733,7 +733,10 @@ template <int NT, int MAXIPT> hipError_t launch_rows(const TopkArgs &a, hipStrea
 } // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
-  if (a.W <= 4096) {
+  // one wave per row pays off once there are rows enough to fill the chip; a
+  // few short rows (a single decode sequence, a prefill tail chunk) finish
+  // sooner with a whole work group each
+  if (a.W <= 4096 && a.R >= 2048) {
     const int groups = (a.R + kRowsPerGroup - 1) / kRowsPerGroup;
     hipLaunchKernelGGL(topk_wave_kernel, dim3(groups), dim3(64 * kRowsPerGroup), 0, s, a);
     return hipGetLastError();
