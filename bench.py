@@ -302,6 +302,42 @@ def prefill_bench(args, torch, idx, synth):
             "tflops_whole_call": flops / (ms * 1e-3) / 1e12}
 
 
+def kv_write_bench(args, torch, idx, synth):
+    """K-cache writer: 65536 new bf16 key rows quantized to FP8 and scattered
+    over a 1024-page pool of 64-row pages (rows in a random slot order)."""
+    import numpy as np
+    P, pages, N = 64, 1024, 65536
+    cache = synth._alloc_cache(synth.FP8, pages, P, 128, None, "separate", False)
+    rng = np.random.default_rng(3)
+    k = torch.from_numpy(rng.standard_normal((N, 128)).astype(np.float32)).to(torch.bfloat16)
+    k = k.cuda()
+    slots = torch.from_numpy(rng.permutation(pages * P)[:N].astype(np.int64)).cuda()
+    data = torch.from_numpy(cache.data).cuda()
+    scale = torch.from_numpy(cache.scale).cuda()
+    kv = idx.make_kv_cache(synth.FP8, P, pages, data, cache.page_stride, cache.row_stride, scale,
+                           cache.scale_page_stride, cache.scale_row_stride)
+
+    def call():
+        idx.idx_kv_cache_write(k, idx.IDX_KIN_BF16, 128, N, slots, kv)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    n = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = N * (128 * 2 + 128 + 4 + 8)  # bf16 row in, FP8 row + scale out, slot
+    return {"workload": "K-cache write: 65536 bf16 rows -> FP8 + fp32 scale, page 64, "
+                        "random slots", "rows": N, "us_per_call": ms * 1e3,
+            "rows_per_s": N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "achieved_gbs": nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(case, budget_s):
     """The CPU oracle on a bounded sample of the decode workload."""
     import numpy as np
@@ -385,6 +421,10 @@ def main():
     if pre:
         log("prefill: %.3f ms per chunked call, %.1f TFLOP/s whole call" % (
             pre["ms_per_call"], pre["tflops_whole_call"]))
+    kvw = None if args.no_prefill else kv_write_bench(args, torch, idx, synth)
+    if kvw:
+        log("kv write: %.1f us per %d rows, %.0f GB/s" % (kvw["us_per_call"], kvw["rows"],
+                                                         kvw["achieved_gbs"]))
     others = []
     if args.all_workloads:
         for wl in (1, 3, 5):
@@ -444,6 +484,8 @@ def main():
             "fp8_tflops_whole_call": pre["tflops_whole_call"],
             "fp8_mfma_frac_whole_call": pre["tflops_whole_call"] / FP8_MFMA_PEAK_TFLOPS,
         }
+    if kvw:
+        line["kv_cache_write"] = kvw
     if others:
         line["other_decode_workloads"] = others
     print(json.dumps(line), flush=True)

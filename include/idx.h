@@ -213,6 +213,41 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
                                     int32_t *cta_scratch, int64_t cta_scratch_ints,
                                     int32_t *out_idx, void *stream);
 
+/* Element type of the key rows idx_kv_cache_write quantizes. */
+typedef enum idx_kin_dtype {
+    IDX_KIN_F32 = 0,
+    IDX_KIN_BF16 = 1
+} idx_kin_dtype;
+
+/*
+ * Indexer K-cache writer: quantizes N new key rows of 128 values to the
+ * cache's storage format and scatters them into their pages, the step that
+ * produces what idx_paged_mqa_logits reads (ATOM PR #1709 names the "FP4
+ * mqa-logits / scatter kernels" in the commit adding the FP4 indexer flag).
+ *   k             device, N rows of 128 fp32 or bf16 (k_dtype), row r at
+ *                 element r*k_row_stride (k_row_stride >= 128)
+ *   slot_mapping  device int64 [N]: row r goes to page slot_mapping[r] / P,
+ *                 slot slot_mapping[r] % P; a negative entry or a page at or
+ *                 past kv->num_pages skips the row (nothing written)
+ *   kv            destination cache (dtype FP8 or MXFP4, same strides as for
+ *                 the scores); its data and scale buffers ARE WRITTEN
+ * Encoding (readings; the pages name the kernels only):
+ *   FP8 E4M3FN: one fp32 scale per row, amax/448 in single precision (1 for
+ *   an all-zero row); codes = x/scale rounded to the nearest E4M3 value, ties
+ *   to the even code, sign kept.
+ *   MXFP4 (OCP MX): per 32 elements the E8M0 exponent floor(log2 amax) - 2,
+ *   clamped to [-127, 127] (0 for an all-zero block); codes = x*2^-e rounded
+ *   to the nearest E2M1 magnitude, ties to the even code, saturating at 6, the
+ *   sign bit only on a nonzero code; the even element in the low nibble.
+ * Rows mapping to the same slot race (the result is one of them).
+ * Errors: IDX_ERR_INVALID (null pointers, N < 0, bad k_dtype or stride, a
+ * cache descriptor that fails the checks of idx_paged_mqa_logits),
+ * IDX_ERR_UNSUPPORTED (cache dtype other than FP8 / MXFP4). N = 0 is a no-op.
+ */
+idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stride, int32_t N,
+                              const int64_t *slot_mapping, const idx_kv_cache *kv,
+                              void *stream);
+
 /* Human-readable name of a status (static string). */
 const char *idx_status_string(idx_status s);
 

@@ -66,6 +66,14 @@ def _load():
         lib.orc_topk_f32.argtypes = [P, i64, i32, P]
         lib.orc_topk_rows_f32.restype = i32
         lib.orc_topk_rows_f32.argtypes = [P, i64, P, i64, i32, P]
+        lib.orc_enc_fp8_e4m3.restype = ctypes.c_uint8
+        lib.orc_enc_fp8_e4m3.argtypes = [ctypes.c_float]
+        lib.orc_quant_fp8_row.restype = None
+        lib.orc_quant_fp8_row.argtypes = [P, i32, P, P]
+        lib.orc_quant_mxfp4_row.restype = None
+        lib.orc_quant_mxfp4_row.argtypes = [P, i32, P, P]
+        lib.orc_kv_write.restype = i32
+        lib.orc_kv_write.argtypes = [i32, P, i64, i64, i32, P, i32, i64, P, i64, i64, P, i64, i64]
         _lib = lib
     return _lib
 
@@ -186,3 +194,42 @@ def topk_rows_f32(logits, E, k):
     if rc != 0:
         raise ValueError("oracle topk_rows failed with code %d" % rc)
     return out
+
+
+def enc_fp8(y: float) -> int:
+    """Nearest E4M3FN code to the single-precision value y (ties to even)."""
+    return int(_load().orc_enc_fp8_e4m3(float(y)))
+
+
+def quant_fp8_row(x):
+    """One row to (FP8 codes uint8 [D], fp32 scale) by the oracle's encoder."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.shape[0], dtype=np.uint8)
+    scale = np.empty(1, dtype=np.float32)
+    _load().orc_quant_fp8_row(_ptr(x), x.shape[0], _ptr(codes), _ptr(scale))
+    return codes, float(scale[0])
+
+
+def quant_mxfp4_row(x):
+    """One row to (packed E2M1 uint8 [D/2], E8M0 scales uint8 [D/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[0]
+    packed = np.empty(D // 2, dtype=np.uint8)
+    scales = np.empty(D // 32, dtype=np.uint8)
+    _load().orc_quant_mxfp4_row(_ptr(x), D, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def kv_write(dtype, k, slot_mapping, cache: Cache):
+    """Quantizes the rows of k (float32 [N, D]) into the cache image in place
+    (cache.data / cache.scale are modified); rows with a negative slot or a
+    page past the pool are skipped."""
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    N, D = k.shape
+    rc = _load().orc_kv_write(dtype, _ptr(k), D, N, D, _ptr(sm), cache.page_size,
+                              cache.num_pages, _ptr(cache.data), cache.page_stride,
+                              cache.row_stride, _ptr(cache.scale), cache.scale_page_stride,
+                              cache.scale_row_stride)
+    if rc != 0:
+        raise ValueError("oracle kv_write failed with code %d" % rc)

@@ -406,3 +406,134 @@ int orc_topk_rows_f32(const float *logits, int64_t W, const int64_t *E,
     }
     return rc_all;
 }
+
+/* --------------------------------------------------------- K-cache writer */
+/*
+ * The step before the scores: new K rows are quantized to the cache's storage
+ * format and scattered into their pages (ATOM PR #1709 names "FP4 mqa-logits /
+ * scatter kernels" in the commit that adds the FP4 indexer flag). The pages do
+ * not print the quantizer; the readings adopted (and used by the input
+ * generator the scoring tests run on) are:
+ *   - FP8: one fp32 scale per row, amax / 448 computed in single precision
+ *     (1 for an all-zero row); codes are the E4M3FN value nearest to
+ *     x / scale (single-precision quotient), ties to the even code, the sign
+ *     kept (so -0 and small negatives give 0x80).
+ *   - MXFP4 (OCP MX): per 32-element block the shared exponent
+ *     e = floor(log2(amax)) - 2 (2 = the largest E2M1 exponent), clamped to
+ *     [-127, 127] (0 for an all-zero block), stored as the E8M0 byte e + 127;
+ *     codes are the E2M1 magnitude nearest to |x| * 2^-e, ties to the even
+ *     code, saturating at 6, with the sign bit set only for a nonzero code;
+ *     the even element goes to the low nibble.
+ * Both encoders search the decoders' value tables: no bit tricks.
+ */
+
+/* Nearest E4M3FN code to y (single precision), ties to the even code. */
+uint8_t orc_enc_fp8_e4m3(float y)
+{
+    const double a = fabs((double)y);
+    int best = 0;
+    double best_d = INFINITY;
+    int c;
+    for (c = 0; c < 0x7F; ++c) { /* 0x7F is NaN */
+        const double v = orc_dec_fp8_e4m3((uint8_t)c);
+        const double d = fabs(v - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* Nearest E2M1 magnitude code (0..7) to a >= 0, ties to the even code,
+ * saturating at the largest magnitude. */
+static int orc_enc_e2m1_mag(double a)
+{
+    int best = 0, c;
+    double best_d = INFINITY;
+    for (c = 0; c < 8; ++c) {
+        const double d = fabs(orc_dec_e2m1((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+/* One row of D values to FP8 codes + fp32 scale. */
+void orc_quant_fp8_row(const float *x, int D, uint8_t *codes, float *scale)
+{
+    float amax = 0.f, s;
+    int i;
+    for (i = 0; i < D; ++i)
+        amax = fabsf(x[i]) > amax ? fabsf(x[i]) : amax;
+    s = amax > 0.f ? amax / 448.0f : 1.0f;
+    for (i = 0; i < D; ++i)
+        codes[i] = orc_enc_fp8_e4m3(x[i] / s);
+    *scale = s;
+}
+
+/* One row of D values (a multiple of 32) to packed E2M1 + E8M0 bytes. */
+void orc_quant_mxfp4_row(const float *x, int D, uint8_t *packed, uint8_t *scales)
+{
+    int b, i;
+    memset(packed, 0, (size_t)D / 2);
+    for (b = 0; b < D / 32; ++b) {
+        const float *blk = x + 32 * b;
+        float amax = 0.f;
+        int e = 0, ex;
+        for (i = 0; i < 32; ++i)
+            amax = fabsf(blk[i]) > amax ? fabsf(blk[i]) : amax;
+        if (amax > 0.f) {
+            (void)frexpf(amax, &ex); /* amax = m * 2^ex, m in [0.5, 1) */
+            e = ex - 1 - 2;
+            e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        }
+        scales[b] = (uint8_t)(e + 127);
+        for (i = 0; i < 32; ++i) {
+            const float y = ldexpf(blk[i], -e);
+            int c = orc_enc_e2m1_mag(fabs((double)y));
+            if (y < 0.f && c > 0)
+                c |= 8;
+            packed[(32 * b + i) / 2] |= (uint8_t)(((i & 1) ? c << 4 : c));
+        }
+    }
+}
+
+/* Writes N rows (row stride ld floats) into a cache image: row t goes to
+ * slot_mapping[t] = page * P + slot (skipped when negative or past the pool),
+ * its bytes at data + page*page_stride + slot*row_stride and its scale at
+ * scale + page*scale_page_stride + slot*scale_row_stride. */
+int orc_kv_write(int dtype, const float *k, int64_t ld, int64_t N, int D,
+                 const int64_t *slot_mapping, int P, int64_t num_pages,
+                 uint8_t *data, int64_t page_stride, int64_t row_stride,
+                 uint8_t *scale, int64_t scale_page_stride, int64_t scale_row_stride)
+{
+    int64_t t;
+    uint8_t codes[256];
+    uint8_t sc[8];
+    if ((dtype != ORC_FP8 && dtype != ORC_MXFP4) || D < 32 || D > 256 || D % 32 || P < 1)
+        return ORC_BAD_ARG;
+    for (t = 0; t < N; ++t) {
+        const int64_t s = slot_mapping[t];
+        int64_t pg, sl;
+        if (s < 0)
+            continue;
+        pg = s / P;
+        sl = s % P;
+        if (pg >= num_pages)
+            continue;
+        if (dtype == ORC_FP8) {
+            float f;
+            orc_quant_fp8_row(k + t * ld, D, codes, &f);
+            memcpy(data + pg * page_stride + sl * row_stride, codes, (size_t)D);
+            memcpy(scale + pg * scale_page_stride + sl * scale_row_stride, &f, 4);
+        } else {
+            orc_quant_mxfp4_row(k + t * ld, D, codes, sc);
+            memcpy(data + pg * page_stride + sl * row_stride, codes, (size_t)D / 2);
+            memcpy(scale + pg * scale_page_stride + sl * scale_row_stride, sc, (size_t)D / 32);
+        }
+    }
+    return ORC_OK;
+}

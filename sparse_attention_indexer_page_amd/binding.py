@@ -23,12 +23,15 @@ IDX_ERR_HIP = 4
 IDX_FP8_E4M3 = 1
 IDX_MXFP4 = 2
 
+IDX_KIN_F32 = 0
+IDX_KIN_BF16 = 1
+
 # Every symbol include/idx.h declares.
 EXPORTS = (
     "idx_schedule_ints", "idx_recommended_ctas", "idx_build_schedule",
     "idx_paged_mqa_logits", "idx_topk_workspace_size", "idx_topk",
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
-    "idx_prefill_schedule_ints", "idx_prefill_chunked_topk",
+    "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_kv_cache_write",
     "idx_status_string", "idx_last_error", "idx_version",
 )
 
@@ -88,6 +91,7 @@ def load(path: str = LIB_PATH):
         "idx_prefill_schedule_ints": (i64, [i32, i64, i64]),
         "idx_prefill_chunked_topk": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P, P,
                                           i32, i64, i64, i32, P, i64, P, i64, P, P]),
+        "idx_kv_cache_write": (st, [P, i32, i64, i32, P, ctypes.POINTER(KVCache), P]),
         "idx_status_string": (ctypes.c_char_p, [st]),
         "idx_last_error": (ctypes.c_char_p, []),
         "idx_version": (i32, []),
@@ -206,3 +210,9 @@ def idx_prefill_chunked_topk(query: Query, kv: KVCache, block_table, visible_end
 def idx_last_error_message() -> str:
     """idx_last_error() of the calling thread."""
     return load().idx_last_error().decode()
+
+
+def idx_kv_cache_write(k, k_dtype, k_row_stride, N, slot_mapping, kv: KVCache, stream=None):
+    _check(load().idx_kv_cache_write(ptr(k), k_dtype, k_row_stride, N, ptr(slot_mapping),
+                                     ctypes.byref(kv), stream_handle(stream)),
+           "idx_kv_cache_write")

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libidx.so")
-SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip"]
+SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip", "kv_write.hip"]
 ARCH = "gfx950"
 
 

@@ -251,6 +251,44 @@ idx_status idx_topk(const float *logits, int64_t W, const int32_t *context_lens,
   return ok();
 }
 
+idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stride, int32_t N,
+                              const int64_t *slot_mapping, const idx_kv_cache *kv,
+                              void *stream) {
+  if (!kv) return fail(IDX_ERR_INVALID, "kv cache descriptor is null");
+  if (kv->dtype != IDX_FP8_E4M3 && kv->dtype != IDX_MXFP4)
+    return fail(IDX_ERR_UNSUPPORTED, "cache dtype %d is neither FP8 nor MXFP4", kv->dtype);
+  idx_status st;
+  if ((st = check_cache(kv, kv->dtype)) != IDX_OK) return st;
+  if (N < 0) return fail(IDX_ERR_INVALID, "N = %d must be >= 0", N);
+  if (k_dtype != IDX_KIN_F32 && k_dtype != IDX_KIN_BF16)
+    return fail(IDX_ERR_INVALID, "k_dtype %d is neither fp32 nor bf16", k_dtype);
+  if (k_row_stride < idx::kHeadDim)
+    return fail(IDX_ERR_INVALID, "k_row_stride %lld below the %d-value row",
+                (long long)k_row_stride, idx::kHeadDim);
+  if (N == 0) return ok();
+  if (!k || !slot_mapping) return fail(IDX_ERR_INVALID, "null k or slot_mapping");
+  if (!aligned(k, k_dtype == IDX_KIN_F32 ? 4 : 2) || !aligned(slot_mapping, 8))
+    return fail(IDX_ERR_INVALID, "k or slot_mapping misaligned for its element type");
+  idx::KvWriteArgs a;
+  a.k = k;
+  a.k_bf16 = k_dtype == IDX_KIN_BF16;
+  a.k_row_stride = k_row_stride;
+  a.N = N;
+  a.slot_mapping = slot_mapping;
+  a.dtype = kv->dtype;
+  a.data = static_cast<uint8_t *>(const_cast<void *>(kv->data));
+  a.page_stride = kv->page_stride_bytes;
+  a.row_stride = kv->row_stride_bytes;
+  a.scale = static_cast<uint8_t *>(const_cast<void *>(kv->scale));
+  a.scale_page_stride = kv->scale_page_stride_bytes;
+  a.scale_row_stride = kv->scale_row_stride_bytes;
+  a.num_pages = kv->num_pages;
+  a.page_size = kv->page_size;
+  hipError_t e = idx::launch_kv_write(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv write launch");
+  return ok();
+}
+
 int64_t idx_prefill_rows_per_chunk(int64_t W, int64_t budget_bytes) {
   if (W < 1) return 0;
   return prefill_rows_per_chunk(W, budget_bytes);

@@ -84,7 +84,25 @@ struct TopkArgs {
   int32_t *out_count; // [R] or null
 };
 
+struct KvWriteArgs {
+  const void *k;       // [N][128] fp32 or bf16 rows
+  int32_t k_bf16;      // 1: bf16 input, 0: fp32
+  int64_t k_row_stride; // elements between rows
+  int32_t N;
+  const int64_t *slot_mapping; // [N]: page * P + slot, < 0 skips the row
+  int32_t dtype;       // IDX_FP8_E4M3 / IDX_MXFP4 (cache format)
+  uint8_t *data;
+  int64_t page_stride;
+  int64_t row_stride;
+  uint8_t *scale;
+  int64_t scale_page_stride;
+  int64_t scale_row_stride;
+  int64_t num_pages;
+  int32_t page_size;
+};
+
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_logits_fp8_decode(const LogitsArgs &a, hipStream_t s);
 hipError_t launch_logits_mxfp4_decode(const LogitsArgs &a, hipStream_t s);
 hipError_t launch_logits_fp8_prefill(const LogitsArgs &a, hipStream_t s);

@@ -1,0 +1,124 @@
+// Indexer K-cache writer on gfx950: new key rows are quantized to the cache's
+// storage format and scattered into their pages (ROCm/ATOM PR #1709 names the
+// "FP4 mqa-logits / scatter kernels" in the commit adding the FP4 indexer
+// flag; the scores read exactly what this writes).
+//
+// One wave per row of 128 values, two per lane (elements 2l and 2l+1):
+//   * FP8 E4M3FN: one fp32 scale per row, amax / 448 (1 for an all-zero row);
+//     each code is x / scale rounded to the nearest E4M3 value, ties to the
+//     even code, sign kept. Lane l stores bytes 2l, 2l+1 (a coalesced 128-byte
+//     row) and lane 0 the scale.
+//   * MXFP4 (OCP MX): per 32-element block (16 lanes) the shared exponent
+//     e = floor(log2 amax) - 2 (the largest E2M1 exponent), clamped to
+//     [-127, 127], 0 for an all-zero block; codes are |x| * 2^-e rounded to the
+//     nearest E2M1 magnitude, ties to the even code, saturating at 6, sign only
+//     on a nonzero code. Lane l stores byte l (element 2l in the low nibble);
+//     lane 0 stores the four E8M0 bytes.
+// slot_mapping[t] = page * P + slot places row t; a negative slot or a page
+// outside the pool skips the row (nothing is written).
+#include "device_common.h"
+#include "internal.h"
+
+namespace idx {
+namespace {
+
+using namespace dev;
+
+constexpr int kRowsPerGroup = 4; // waves (rows) per work group
+
+__device__ inline float load_k(const KvWriteArgs &a, int64_t i) {
+  if (a.k_bf16) {
+    const uint16_t h = reinterpret_cast<const uint16_t *>(a.k)[i];
+    return __uint_as_float((uint32_t)h << 16);
+  }
+  return reinterpret_cast<const float *>(a.k)[i];
+}
+
+// Nearest E4M3FN code to y (|y| <= 448 up to rounding), ties to the even code.
+__device__ inline uint32_t fp8_e4m3_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // subnormal range: multiples of 2^-9; rintf rounds half to even
+    code = (uint32_t)rintf(a * 512.0f); // 8 means the smallest normal, 0x08
+  } else {
+    // normal: keep 3 mantissa bits of the fp32 pattern, round half to even
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t lsb = (ab >> 20) & 1u;
+    const uint32_t r = ab + 0x7FFFFu + lsb;        // may carry into the exponent
+    const uint32_t exp = (r >> 23) - 127 + 7;      // E4M3 biased exponent
+    code = (exp << 3) | ((r >> 20) & 7u);
+    if (code > 0x7Eu) code = 0x7Eu; // saturate at 448
+  }
+  return code | sign;
+}
+
+// Nearest E2M1 magnitude code (0..7) to a >= 0, ties to the even code,
+// saturating at 6.
+__device__ inline uint32_t e2m1_rne(float a) {
+  return (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+         (a > 5.0f);
+}
+
+__global__ __launch_bounds__(64 * kRowsPerGroup) void kv_write_kernel(KvWriteArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kRowsPerGroup + wave;
+  if (t >= a.N) return;
+  const int64_t slot = uniform_load(a.slot_mapping + t);
+  if (slot < 0) return;
+  const int64_t pg = slot / a.page_size;
+  const int64_t sl = slot - pg * a.page_size;
+  if (pg >= a.num_pages) return;
+  const int64_t base = (int64_t)t * a.k_row_stride;
+  const float x0 = load_k(a, base + 2 * lane);
+  const float x1 = load_k(a, base + 2 * lane + 1);
+  uint8_t *row = a.data + pg * a.page_stride + sl * a.row_stride;
+  uint8_t *srow = a.scale + pg * a.scale_page_stride + sl * a.scale_row_stride;
+  float m = fmaxf(fabsf(x0), fabsf(x1));
+  if (a.dtype == IDX_FP8_E4M3) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float s = m > 0.f ? m / 448.0f : 1.0f;
+    const uint32_t c0 = fp8_e4m3_rne(x0 / s), c1 = fp8_e4m3_rne(x1 / s);
+    reinterpret_cast<uint16_t *>(row)[lane] = (uint16_t)(c0 | (c1 << 8));
+    if (lane == 0) *reinterpret_cast<float *>(srow) = s;
+  } else {
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64)); // 16-lane block
+    int e = 0;
+    if (m > 0.f) {
+      int ex;
+      (void)frexpf(m, &ex); // m = f * 2^ex, f in [0.5, 1)
+      e = ex - 1 - 2;
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    const float y0 = ldexpf(x0, -e), y1 = ldexpf(x1, -e);
+    uint32_t c0 = e2m1_rne(fabsf(y0)), c1 = e2m1_rne(fabsf(y1));
+    if (y0 < 0.f && c0) c0 |= 8u;
+    if (y1 < 0.f && c1) c1 |= 8u;
+    row[lane] = (uint8_t)(c0 | (c1 << 4));
+    const uint32_t sb = (uint32_t)(e + 127);
+    const uint32_t s0 = __builtin_amdgcn_readlane(sb, 0), s1 = __builtin_amdgcn_readlane(sb, 16);
+    const uint32_t s2 = __builtin_amdgcn_readlane(sb, 32), s3 = __builtin_amdgcn_readlane(sb, 48);
+    if (lane == 0) {
+      srow[0] = (uint8_t)s0;
+      srow[1] = (uint8_t)s1;
+      srow[2] = (uint8_t)s2;
+      srow[3] = (uint8_t)s3;
+    }
+  }
+}
+
+} // namespace
+
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s) {
+  if (a.N <= 0) return hipSuccess;
+  const int groups = (a.N + kRowsPerGroup - 1) / kRowsPerGroup;
+  hipLaunchKernelGGL(kv_write_kernel, dim3(groups), dim3(64 * kRowsPerGroup), 0, s, a);
+  return hipGetLastError();
+}
+
+} // namespace idx

@@ -179,3 +179,32 @@ def test_prefill_rejects_small_scratch(lib):
     rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
                                       1 << 20, 16, 0x300, 1 << 30, 0x400, 2, 0x500, None)
     assert rc == idx.IDX_ERR_WORKSPACE
+
+
+def _kvw(k=0x8000, kd=0, ld=128, N=4, sm=0x9000, kv=None):
+    kv = kv if kv is not None else _kv()
+    return idx.load().idx_kv_cache_write(k, kd, ld, N, sm, ctypes.byref(kv), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), idx.IDX_ERR_INVALID),
+    (dict(sm=0), idx.IDX_ERR_INVALID),
+    (dict(kd=2), idx.IDX_ERR_INVALID),
+    (dict(ld=127), idx.IDX_ERR_INVALID),
+    (dict(N=-1), idx.IDX_ERR_INVALID),
+    (dict(k=0x8002), idx.IDX_ERR_INVALID),          # fp32 rows need 4-byte alignment
+    (dict(sm=0x9004), idx.IDX_ERR_INVALID),         # int64 slots need 8-byte alignment
+    (dict(kv=_kv(dtype=7)), idx.IDX_ERR_UNSUPPORTED),
+    (dict(kv=_kv(P=48)), idx.IDX_ERR_INVALID),
+    (dict(kv=_kv(data=0)), idx.IDX_ERR_INVALID),
+    (dict(kv=_kv(rs=112)), idx.IDX_ERR_INVALID),
+])
+def test_kv_write_rejects_bad_arguments(lib, kw, status):
+    assert _kvw(**kw) == status
+    assert idx.idx_last_error_message() != ""
+
+
+def test_kv_write_of_no_rows_is_a_no_op(lib):
+    # N = 0 launches nothing, so it succeeds without touching the (fake) pointers
+    assert _kvw(k=0, sm=0, N=0) == idx.IDX_OK
+    assert _kvw(k=0x8002, kd=1, N=0) == idx.IDX_OK

@@ -383,3 +383,116 @@ def test_topk_rows_f32_matches_per_row():
     out = oracle.topk_rows_f32(lg, E, 16)
     for i in range(5):
         assert np.array_equal(out[i], _lexsort_topk(lg[i], E[i], 16))
+
+
+# ------------------------------------------------------------ K-cache writer
+
+def _e4m3_values():
+    return np.array([oracle.dec_fp8(c) for c in range(0x7F)])  # 0..448, no NaN
+
+
+def test_fp8_encoder_matches_torch_cast():
+    """The oracle's E4M3 encoder (nearest by table search, ties to even) equals
+    torch's float8_e4m3fn cast on representable values, midpoints (ties),
+    near-midpoints, subnormals and random values, both signs."""
+    v = _e4m3_values()
+    mids = (v[1:] + v[:-1]) / 2
+    rng = np.random.default_rng(5)
+    ys = np.concatenate([v, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                         np.nextafter(mids.astype(np.float32), np.float32(1e9)),
+                         rng.standard_normal(2000) * 50, rng.uniform(0, 2 ** -6, 500)])
+    ys = ys[np.abs(ys) <= 448].astype(np.float32)
+    ys = np.concatenate([ys, -ys])
+    want = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.enc_fp8(float(y)) for y in ys], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_fp8_row_quantizer_bounds():
+    """Per-row FP8: the largest magnitude maps to 448 exactly, every value is
+    within half a code step of x/scale, and an all-zero row has scale 1."""
+    rng = np.random.default_rng(6)
+    for scale in (1e-3, 1.0, 37.0):
+        x = (rng.standard_normal(128) * scale).astype(np.float32)
+        codes, s = oracle.quant_fp8_row(x)
+        vals = np.array([oracle.dec_fp8(int(c)) for c in codes])
+        assert np.max(np.abs(vals)) == 448.0
+        y = x.astype(np.float64) / s
+        step = np.where(np.abs(y) < 2 ** -6, 2.0 ** -9,
+                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 2 ** -6))) - 3))
+        assert np.all(np.abs(vals - y) <= step / 2 + 1e-12)
+    codes, s = oracle.quant_fp8_row(np.zeros(128, np.float32))
+    assert s == 1.0 and not codes.any()
+
+
+def test_mxfp4_encoder_is_nearest_with_even_ties():
+    """Per 32-element block: the block maximum scales into [4, 8), every code is
+    the nearest E2M1 magnitude of |x|*2^-e (distance checked against all eight),
+    an exact tie takes the even code, and zero never carries a sign."""
+    mags = np.array([oracle.dec_e2m1(c) for c in range(8)])
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(256) * 3).astype(np.float32)
+    x[:8] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.0]   # ties after e = 0 scaling
+    x[8] = 7.9
+    packed, sc = oracle.quant_mxfp4_row(x)
+    codes = np.empty(256, dtype=np.int64)
+    codes[0::2], codes[1::2] = packed & 15, packed >> 4
+    for b in range(8):
+        e = int(sc[b]) - 127
+        y = x[32 * b:32 * b + 32].astype(np.float64) * 2.0 ** -e
+        if b > 0:
+            assert 4 <= np.max(np.abs(y)) < 8
+        for i in range(32):
+            c = int(codes[32 * b + i])
+            mag = c & 7
+            d = np.abs(mags - min(abs(y[i]), 1e300))
+            assert d[mag] == d.min()
+            if np.sum(d == d.min()) > 1:
+                assert mag % 2 == 0
+            assert (c & 8) == (8 if (y[i] < 0 and mag > 0) else 0)
+    # block 0 holds 7.9 -> e = 0: the ties above resolve to the even codes
+    assert list(codes[:7] & 7) == [0, 2, 2, 4, 4, 6, 6]
+
+
+def test_writer_encoders_agree_with_the_input_generator():
+    """The oracle's encoders give the same bytes as the generator the scoring
+    tests run on (an independent implementation: torch cast / thresholds)."""
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((20, 128)) * rng.uniform(1e-3, 50, (20, 1))).astype(np.float32)
+    x[3] = 0.0
+    x[4, 5] = -0.0
+    codes, scales = synth.quantize_fp8_rows(x)
+    packed, sc = synth.quantize_mxfp4(x)
+    for r in range(20):
+        c, s = oracle.quant_fp8_row(x[r])
+        assert np.array_equal(c, codes[r]) and np.float32(s) == scales[r]
+        p, e = oracle.quant_mxfp4_row(x[r])
+        assert np.array_equal(p, packed[r]) and np.array_equal(e, sc[r])
+
+
+def test_oracle_kv_write_scatters_and_skips():
+    """Rows land at page*P + slot of their slot_mapping entry with their own
+    quantized bytes; a negative slot or a page past the pool writes nothing."""
+    P, pages = 32, 4
+    for dtype, db in ((synth.FP8, 128), (synth.MXFP4, 64)):
+        cache = synth._alloc_cache(dtype, pages, P, 128, None, "separate", True)
+        data0, scale0 = cache.data.copy(), cache.scale.copy()
+        rng = np.random.default_rng(9)
+        k = rng.standard_normal((6, 128)).astype(np.float32)
+        sm = np.array([5, -1, 3 * P + 31, pages * P, 0, 40])
+        oracle.kv_write(dtype, k, sm, oracle.Cache(dtype, cache.data, cache.page_stride,
+                                                   cache.row_stride, cache.scale,
+                                                   cache.scale_page_stride,
+                                                   cache.scale_row_stride, P, pages))
+        touched = np.zeros(cache.data.shape, bool)
+        for t, s in enumerate(sm):
+            if s < 0 or s >= pages * P:
+                continue
+            want = oracle.quant_fp8_row(k[t])[0] if dtype == synth.FP8 else \
+                oracle.quant_mxfp4_row(k[t])[0]
+            off = (s // P) * cache.page_stride + (s % P) * cache.row_stride
+            assert np.array_equal(cache.data[off:off + db], want)
+            touched[off:off + db] = True
+        assert np.array_equal(cache.data[~touched], data0[~touched])
+        changed_scales = np.nonzero(cache.scale != scale0)[0] // 4
+        assert set(changed_scales.tolist()) <= {5, 3 * P + 31, 0, 40}
