@@ -225,7 +225,8 @@ typedef enum idx_kin_dtype {
  * produces what idx_paged_mqa_logits reads (ATOM PR #1709 names the "FP4
  * mqa-logits / scatter kernels" in the commit adding the FP4 indexer flag).
  *   k             device, N rows of 128 fp32 or bf16 (k_dtype), row r at
- *                 element r*k_row_stride (k_row_stride >= 128)
+ *                 element r*k_row_stride (k_row_stride >= 128 and even; k
+ *                 aligned to two elements: 8 bytes fp32, 4 bytes bf16)
  *   slot_mapping  device int64 [N]: row r goes to page slot_mapping[r] / P,
  *                 slot slot_mapping[r] % P; a negative entry or a page at or
  *                 past kv->num_pages skips the row (nothing written)

@@ -267,8 +267,11 @@ idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stri
                 (long long)k_row_stride, idx::kHeadDim);
   if (N == 0) return ok();
   if (!k || !slot_mapping) return fail(IDX_ERR_INVALID, "null k or slot_mapping");
-  if (!aligned(k, k_dtype == IDX_KIN_F32 ? 4 : 2) || !aligned(slot_mapping, 8))
-    return fail(IDX_ERR_INVALID, "k or slot_mapping misaligned for its element type");
+  // rows are read two values at a time: 8-byte (fp32) / 4-byte (bf16) alignment
+  const size_t pair = k_dtype == IDX_KIN_F32 ? 8 : 4;
+  if (!aligned(k, pair) || k_row_stride % 2 || !aligned(slot_mapping, 8))
+    return fail(IDX_ERR_INVALID, "k (pairs of values), k_row_stride (even) or slot_mapping "
+                                 "misaligned");
   idx::KvWriteArgs a;
   a.k = k;
   a.k_bf16 = k_dtype == IDX_KIN_BF16;
@@ -283,7 +286,7 @@ idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stri
   a.scale_page_stride = kv->scale_page_stride_bytes;
   a.scale_row_stride = kv->scale_row_stride_bytes;
   a.num_pages = kv->num_pages;
-  a.page_size = kv->page_size;
+  a.page_shift = kv->page_size == 32 ? 5 : (kv->page_size == 64 ? 6 : 8);
   hipError_t e = idx::launch_kv_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv write launch");
   return ok();

@@ -98,7 +98,7 @@ struct KvWriteArgs {
   int64_t scale_page_stride;
   int64_t scale_row_stride;
   int64_t num_pages;
-  int32_t page_size;
+  int32_t page_shift; // log2 of the page size
 };
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);

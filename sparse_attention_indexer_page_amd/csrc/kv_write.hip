@@ -24,14 +24,20 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRowsPerGroup = 4; // waves (rows) per work group
+constexpr int kRowsPerGroup = 4; // waves per work group
+constexpr int kRowsPerWave = 4;
 
-__device__ inline float load_k(const KvWriteArgs &a, int64_t i) {
+// Elements i and i+1 (i even) of the input, as fp32, with one load.
+__device__ inline void load_pair(const KvWriteArgs &a, int64_t i, float &x0, float &x1) {
   if (a.k_bf16) {
-    const uint16_t h = reinterpret_cast<const uint16_t *>(a.k)[i];
-    return __uint_as_float((uint32_t)h << 16);
+    const uint32_t h = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(a.k) + i);
+    x0 = __uint_as_float(h << 16);
+    x1 = __uint_as_float(h & 0xFFFF0000u);
+  } else {
+    const float2 v = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(a.k) + i);
+    x0 = v.x;
+    x1 = v.y;
   }
-  return reinterpret_cast<const float *>(a.k)[i];
 }
 
 // Nearest E4M3FN code to y (|y| <= 448 up to rounding), ties to the even code.
@@ -62,19 +68,13 @@ __device__ inline uint32_t e2m1_rne(float a) {
          (a > 5.0f);
 }
 
-__global__ __launch_bounds__(64 * kRowsPerGroup) void kv_write_kernel(KvWriteArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Quantizes one row (x0, x1 = this lane's two values) into its slot.
+__device__ inline void write_row(const KvWriteArgs &a, int64_t slot, float x0, float x1) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kRowsPerGroup + wave;
-  if (t >= a.N) return;
-  const int64_t slot = uniform_load(a.slot_mapping + t);
   if (slot < 0) return;
-  const int64_t pg = slot / a.page_size;
-  const int64_t sl = slot - pg * a.page_size;
+  const int64_t pg = slot >> a.page_shift;
+  const int64_t sl = slot & ((1 << a.page_shift) - 1);
   if (pg >= a.num_pages) return;
-  const int64_t base = (int64_t)t * a.k_row_stride;
-  const float x0 = load_k(a, base + 2 * lane);
-  const float x1 = load_k(a, base + 2 * lane + 1);
   uint8_t *row = a.data + pg * a.page_stride + sl * a.row_stride;
   uint8_t *srow = a.scale + pg * a.scale_page_stride + sl * a.scale_row_stride;
   float m = fmaxf(fabsf(x0), fabsf(x1));
@@ -112,11 +112,31 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void kv_write_kernel(KvWriteArg
   }
 }
 
+// Each wave takes kRowsPerWave consecutive rows and loads all of them before
+// quantizing any, so the load latency is paid once per group of rows.
+__global__ __launch_bounds__(64 * kRowsPerGroup) void kv_write_kernel(KvWriteArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * kRowsPerGroup + wave) * kRowsPerWave;
+  if (t0 >= a.N) return;
+  float x0[kRowsPerWave], x1[kRowsPerWave];
+  int64_t slot[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int t = t0 + j < a.N ? t0 + j : a.N - 1; // past the end: reload the last row
+    load_pair(a, (int64_t)t * a.k_row_stride + 2 * lane, x0[j], x1[j]);
+    slot[j] = t0 + j < a.N ? uniform_load(a.slot_mapping + t) : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) write_row(a, slot[j], x0[j], x1[j]);
+}
+
 } // namespace
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  const int groups = (a.N + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int per_group = kRowsPerGroup * kRowsPerWave;
+  const int groups = (a.N + per_group - 1) / per_group;
   hipLaunchKernelGGL(kv_write_kernel, dim3(groups), dim3(64 * kRowsPerGroup), 0, s, a);
   return hipGetLastError();
 }

@@ -192,7 +192,9 @@ def _kvw(k=0x8000, kd=0, ld=128, N=4, sm=0x9000, kv=None):
     (dict(kd=2), idx.IDX_ERR_INVALID),
     (dict(ld=127), idx.IDX_ERR_INVALID),
     (dict(N=-1), idx.IDX_ERR_INVALID),
-    (dict(k=0x8002), idx.IDX_ERR_INVALID),          # fp32 rows need 4-byte alignment
+    (dict(k=0x8004), idx.IDX_ERR_INVALID),          # fp32 pairs need 8-byte alignment
+    (dict(k=0x8002, kd=1), idx.IDX_ERR_INVALID),    # bf16 pairs need 4-byte alignment
+    (dict(ld=129), idx.IDX_ERR_INVALID),            # odd row stride
     (dict(sm=0x9004), idx.IDX_ERR_INVALID),         # int64 slots need 8-byte alignment
     (dict(kv=_kv(dtype=7)), idx.IDX_ERR_UNSUPPORTED),
     (dict(kv=_kv(P=48)), idx.IDX_ERR_INVALID),
