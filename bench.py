@@ -338,6 +338,42 @@ def kv_write_bench(args, torch, idx, synth):
             "achieved_gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
+def q_quant_bench(args, torch, idx, R_decode):
+    """Query quantization with the weight fold: bf16 query rows of 64 x 128
+    to FP8 codes with the row scale folded into the weights, for the decode
+    batch's rows and for a 16384-row prefill batch."""
+    import numpy as np
+    rng = np.random.default_rng(4)
+    res = []
+    for R in (R_decode, 16384):
+        x = torch.from_numpy(rng.standard_normal((R, 8192), dtype=np.float32)).to(torch.bfloat16)
+        x = x.cuda()
+        w = torch.randn((R, 64), dtype=torch.float32, device="cuda")
+        q = torch.empty((R, 8192), dtype=torch.uint8, device="cuda")
+        wo = torch.empty((R, 64), dtype=torch.float32, device="cuda")
+        out = idx.make_query(idx.IDX_FP8_E4M3, q, None, wo)
+
+        def call():
+            idx.idx_quantize_query(x, idx.IDX_KIN_BF16, 8192, R, w, 0.0883883, out)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        nbytes = R * (8192 * 2 + 8192 + 64 * 4 * 2)  # bf16 in, FP8 out, weights in + out
+        res.append({"rows": R, "us_per_call": ms * 1e3, "algorithmic_bytes": nbytes,
+                    "achieved_gbs": nbytes / (ms * 1e-3) / 1e9})
+    return {"workload": "query quantization: bf16 [R][64][128] -> FP8 with the row scale "
+                        "folded into the weights", "runs": res}
+
+
 def cpu_baseline(case, budget_s):
     """The CPU oracle on a bounded sample of the decode workload."""
     import numpy as np
@@ -425,6 +461,12 @@ def main():
     if kvw:
         log("kv write: %.1f us per %d rows, %.0f GB/s" % (kvw["us_per_call"], kvw["rows"],
                                                          kvw["achieved_gbs"]))
+    qq = None
+    if not args.no_prefill:
+        qq = q_quant_bench(args, torch, idx, d["case"].R)
+        for r in qq["runs"]:
+            log("query quantization: %.1f us per %d rows, %.0f GB/s" % (
+                r["us_per_call"], r["rows"], r["achieved_gbs"]))
     others = []
     if args.all_workloads:
         for wl in (1, 3, 5):
@@ -486,6 +528,8 @@ def main():
         }
     if kvw:
         line["kv_cache_write"] = kvw
+    if qq:
+        line["query_quantization"] = qq
     if others:
         line["other_decode_workloads"] = others
     print(json.dumps(line), flush=True)

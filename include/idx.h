@@ -213,7 +213,8 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
                                     int32_t *cta_scratch, int64_t cta_scratch_ints,
                                     int32_t *out_idx, void *stream);
 
-/* Element type of the key rows idx_kv_cache_write quantizes. */
+/* Element type of the rows idx_kv_cache_write and idx_quantize_query
+ * quantize. */
 typedef enum idx_kin_dtype {
     IDX_KIN_F32 = 0,
     IDX_KIN_BF16 = 1
@@ -248,6 +249,41 @@ typedef enum idx_kin_dtype {
 idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stride, int32_t N,
                               const int64_t *slot_mapping, const idx_kv_cache *kv,
                               void *stream);
+
+/*
+ * Indexer query quantization with the weight fold: turns R rows of 64 x 128
+ * query values into the query operands of idx_paged_mqa_logits, the step the
+ * pages call forward_pre's "quant + weights" (ATOM PR #1709, commit on the
+ * forward_pre / score_topk_from split: the FP8 path hands the scorer only the
+ * quantized q and the weights, the FP4 path also keeps its q scales).
+ *   x      device, R rows of 8192 fp32 or bf16 (x_dtype, idx_kin_dtype), head
+ *          h of row r at element r*x_row_stride + 128*h; x 16-byte aligned,
+ *          x_row_stride >= 8192 and a multiple of 8
+ *   w      device fp32 [R][64], the per-head weights before the fold
+ *   c      finite constant multiplied into every weight (e.g. a softmax
+ *          scale times 64^-0.5); 1 for none
+ *   out    descriptor of the destination query (dtype FP8 or MXFP4, 64
+ *          heads, 128 dims, the layout idx_paged_mqa_logits reads); out->q,
+ *          out->q_scale (when not NULL) and out->weights ARE WRITTEN. out->
+ *          weights may equal w (in place).
+ * Encoding (readings; the pages name the step only):
+ *   FP8 E4M3FN: one scale per row s = amax/448 over its 8192 values in single
+ *   precision (1 for an all-zero row); codes = x/s rounded as the K-cache
+ *   writer rounds. With out->q_scale NULL the scale is folded into the
+ *   weights, weights = (w*s)*c (fp32, in that order; valid because
+ *   max(0, s*y) = s*max(0, y) for s > 0), and the scorer is called with
+ *   q_scale NULL. With out->q_scale set, it receives s and weights = w*c.
+ *   MXFP4: per 32 values the OCP MX exponent and E2M1 codes exactly as the K-
+ *   cache writer encodes a key row, scales to out->q_scale [R][64][4]
+ *   (required; a per-block scale does not fold into a per-head weight);
+ *   weights = w*c.
+ * Errors: IDX_ERR_INVALID (null pointers when R > 0, R < 0, bad x_dtype,
+ * stride or alignment, c not finite, a destination that fails the query
+ * checks of idx_paged_mqa_logits), IDX_ERR_UNSUPPORTED (dtype or shape).
+ * R = 0 is a no-op.
+ */
+idx_status idx_quantize_query(const void *x, int32_t x_dtype, int64_t x_row_stride, int32_t R,
+                              const float *w, float c, const idx_query *out, void *stream);
 
 /* Human-readable name of a status (static string). */
 const char *idx_status_string(idx_status s);

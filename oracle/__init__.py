@@ -74,6 +74,9 @@ def _load():
         lib.orc_quant_mxfp4_row.argtypes = [P, i32, P, P]
         lib.orc_kv_write.restype = i32
         lib.orc_kv_write.argtypes = [i32, P, i64, i64, i32, P, i32, i64, P, i64, i64, P, i64, i64]
+        lib.orc_quantize_query.restype = i32
+        lib.orc_quantize_query.argtypes = [i32, P, i64, i64, i32, i32, P, ctypes.c_float, i32,
+                                           P, P, P]
         _lib = lib
     return _lib
 
@@ -233,3 +236,26 @@ def kv_write(dtype, k, slot_mapping, cache: Cache):
                               cache.scale_row_stride)
     if rc != 0:
         raise ValueError("oracle kv_write failed with code %d" % rc)
+
+
+def quantize_query(dtype, x, w, c=1.0, fold=True):
+    """Query rows x (float32 [R, H, D]) and weights w (float32 [R, H]) to
+    (q codes, q scales, weights): FP8 -> (uint8 [R,H,D], float32 [R] or None
+    when folded, float32 [R,H]); MXFP4 -> (uint8 [R,H,D/2], uint8 [R,H,D/32],
+    float32 [R,H])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    R, H, D = x.shape
+    w_out = np.empty((R, H), dtype=np.float32)
+    if dtype == FP8:
+        q = np.empty((R, H, D), dtype=np.uint8)
+        qs = None if fold else np.empty(R, dtype=np.float32)
+    else:
+        q = np.empty((R, H, D // 2), dtype=np.uint8)
+        qs = np.empty((R, H, D // 32), dtype=np.uint8)
+    rc = _load().orc_quantize_query(dtype, _ptr(x), H * D, R, H, D, _ptr(w), float(c),
+                                    1 if (fold and dtype == FP8) else 0, _ptr(q), _ptr(qs),
+                                    _ptr(w_out))
+    if rc != 0:
+        raise ValueError("oracle quantize_query failed with code %d" % rc)
+    return q, qs, w_out

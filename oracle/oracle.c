@@ -537,3 +537,41 @@ int orc_kv_write(int dtype, const float *k, int64_t ld, int64_t N, int D,
     }
     return ORC_OK;
 }
+
+/* ---- Query quantization with the weight fold (ATOM PR #1709, commit on the
+ * forward_pre / score_topk_from split: forward_pre returns the quantized q and
+ * the weights; the FP4 path keeps its q scales beside them).
+ * Readings: FP8 takes one scale per query row over all H*D values (the row
+ * quantizer above on a row of H*D); with fold != 0 that scale goes into the
+ * weights, w_out = (w*s)*c in single precision, and q_scale is not written;
+ * otherwise q_scale[r] = s and w_out = w*c. MXFP4 takes the block quantizer
+ * above on the row of H*D values (blocks of 32 never straddle a head since D
+ * is a multiple of 32) and w_out = w*c. */
+int orc_quantize_query(int dtype, const float *x, int64_t ld, int64_t R, int H, int D,
+                       const float *w, float c, int fold, uint8_t *q, void *q_scale,
+                       float *w_out)
+{
+    int64_t r;
+    int h;
+    const int n = H * D;
+    if (dtype != ORC_FP8 && dtype != ORC_MXFP4)
+        return ORC_BAD_ARG;
+    if (n % 32 || R < 0)
+        return ORC_BAD_ARG;
+    for (r = 0; r < R; ++r) {
+        const float *xr = x + r * ld;
+        if (dtype == ORC_FP8) {
+            float s;
+            orc_quant_fp8_row(xr, n, q + r * n, &s);
+            for (h = 0; h < H; ++h)
+                w_out[r * H + h] = fold ? (w[r * H + h] * s) * c : w[r * H + h] * c;
+            if (!fold)
+                ((float *)q_scale)[r] = s;
+        } else {
+            orc_quant_mxfp4_row(xr, n, q + r * (n / 2), (uint8_t *)q_scale + r * (n / 32));
+            for (h = 0; h < H; ++h)
+                w_out[r * H + h] = w[r * H + h] * c;
+        }
+    }
+    return ORC_OK;
+}

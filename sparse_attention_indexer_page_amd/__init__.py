@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     idx_build_schedule, idx_kv_cache_write,
     idx_last_error_message, idx_paged_mqa_logits, idx_prefill_chunked_topk,
     idx_prefill_rows_per_chunk, idx_prefill_schedule_ints, idx_prefill_scratch_bytes,
-    idx_recommended_ctas, idx_schedule_ints, idx_topk, idx_topk_workspace_size, idx_version,
+    idx_quantize_query, idx_recommended_ctas, idx_schedule_ints, idx_topk,
+    idx_topk_workspace_size, idx_version,
     load, make_kv_cache, make_query, ptr, stream_handle,
 )

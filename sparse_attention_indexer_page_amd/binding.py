@@ -32,7 +32,7 @@ EXPORTS = (
     "idx_paged_mqa_logits", "idx_topk_workspace_size", "idx_topk",
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
     "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_kv_cache_write",
-    "idx_status_string", "idx_last_error", "idx_version",
+    "idx_quantize_query", "idx_status_string", "idx_last_error", "idx_version",
 )
 
 
@@ -92,6 +92,8 @@ def load(path: str = LIB_PATH):
         "idx_prefill_chunked_topk": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P, P,
                                           i32, i64, i64, i32, P, i64, P, i64, P, P]),
         "idx_kv_cache_write": (st, [P, i32, i64, i32, P, ctypes.POINTER(KVCache), P]),
+        "idx_quantize_query": (st, [P, i32, i64, i32, P, ctypes.c_float,
+                                    ctypes.POINTER(Query), P]),
         "idx_status_string": (ctypes.c_char_p, [st]),
         "idx_last_error": (ctypes.c_char_p, []),
         "idx_version": (i32, []),
@@ -216,3 +218,9 @@ def idx_kv_cache_write(k, k_dtype, k_row_stride, N, slot_mapping, kv: KVCache, s
     _check(load().idx_kv_cache_write(ptr(k), k_dtype, k_row_stride, N, ptr(slot_mapping),
                                      ctypes.byref(kv), stream_handle(stream)),
            "idx_kv_cache_write")
+
+
+def idx_quantize_query(x, x_dtype, x_row_stride, R, w, c, out: Query, stream=None):
+    _check(load().idx_quantize_query(ptr(x), x_dtype, x_row_stride, R, ptr(w), c,
+                                     ctypes.byref(out), stream_handle(stream)),
+           "idx_quantize_query")

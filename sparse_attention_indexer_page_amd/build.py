@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libidx.so")
-SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip", "kv_write.hip"]
+SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip", "kv_write.hip",
+           "q_quant.hip"]
 ARCH = "gfx950"
 
 

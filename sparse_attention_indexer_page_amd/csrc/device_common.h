@@ -54,6 +54,47 @@ template <typename T> __device__ inline T uniform_load(const T *p) {
   return *(const __attribute__((address_space(4))) T *)p;
 }
 
+// Storage-format encoders shared by the K-cache writer and the query
+// quantizer (see those kernels for the per-row / per-block scale rules).
+// Nearest E4M3FN code to y (|y| <= 448 up to rounding), ties to the even code.
+__device__ inline uint32_t fp8_e4m3_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // subnormal range: multiples of 2^-9; rintf rounds half to even
+    code = (uint32_t)rintf(a * 512.0f); // 8 means the smallest normal, 0x08
+  } else {
+    // normal: keep 3 mantissa bits of the fp32 pattern, round half to even
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t lsb = (ab >> 20) & 1u;
+    const uint32_t r = ab + 0x7FFFFu + lsb;        // may carry into the exponent
+    const uint32_t exp = (r >> 23) - 127 + 7;      // E4M3 biased exponent
+    code = (exp << 3) | ((r >> 20) & 7u);
+    if (code > 0x7Eu) code = 0x7Eu; // saturate at 448
+  }
+  return code | sign;
+}
+
+// Nearest E2M1 magnitude code (0..7) to a >= 0, ties to the even code,
+// saturating at 6.
+__device__ inline uint32_t e2m1_rne(float a) {
+  return (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+         (a > 5.0f);
+}
+
+// OCP MX shared exponent of a block with magnitude maximum m:
+// floor(log2 m) - 2 (2 = the largest E2M1 exponent), clamped to [-127, 127];
+// 0 for an all-zero block. The E8M0 byte is the result + 127.
+__device__ inline int mx_block_exponent(float m) {
+  if (!(m > 0.f)) return 0;
+  int ex;
+  (void)frexpf(m, &ex); // m = f * 2^ex, f in [0.5, 1)
+  const int e = ex - 1 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 __device__ inline v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // Sum over lane groups g = lane >> 4 of per-lane partials p[t] (one per tile),

@@ -1,6 +1,7 @@
 // C ABI of the indexer library: host-side validation and kernel dispatch.
 // Every check here runs before any HIP call, so a rejected call leaves the
 // device untouched; nothing here allocates, frees or synchronizes.
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -289,6 +290,46 @@ idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stri
   a.page_shift = kv->page_size == 32 ? 5 : (kv->page_size == 64 ? 6 : 8);
   hipError_t e = idx::launch_kv_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv write launch");
+  return ok();
+}
+
+idx_status idx_quantize_query(const void *x, int32_t x_dtype, int64_t x_row_stride, int32_t R,
+                              const float *w, float c, const idx_query *out, void *stream) {
+  if (!out) return fail(IDX_ERR_INVALID, "query descriptor is null");
+  if (out->dtype != IDX_FP8_E4M3 && out->dtype != IDX_MXFP4)
+    return fail(IDX_ERR_UNSUPPORTED, "query dtype %d is not FP8_E4M3 (1) or MXFP4 (2)",
+                out->dtype);
+  if (out->num_heads != idx::kHeads || out->head_dim != idx::kHeadDim)
+    return fail(IDX_ERR_UNSUPPORTED, "query shape %d x %d unsupported (64 x 128 only)",
+                out->num_heads, out->head_dim);
+  if (R < 0) return fail(IDX_ERR_INVALID, "R = %d must be >= 0", R);
+  if (x_dtype != IDX_KIN_F32 && x_dtype != IDX_KIN_BF16)
+    return fail(IDX_ERR_INVALID, "x_dtype %d is neither fp32 nor bf16", x_dtype);
+  if (x_row_stride < (int64_t)idx::kHeads * idx::kHeadDim)
+    return fail(IDX_ERR_INVALID, "x_row_stride %lld below the %d-value row",
+                (long long)x_row_stride, idx::kHeads * idx::kHeadDim);
+  if (!std::isfinite(c)) return fail(IDX_ERR_INVALID, "weight constant is not finite");
+  if (R == 0) return ok();
+  idx_status st = check_query(out);
+  if (st != IDX_OK) return st;
+  if (!x || !w) return fail(IDX_ERR_INVALID, "null x or w");
+  // eight values per load: 16-byte aligned rows
+  if (!aligned(x, 16) || x_row_stride % 8)
+    return fail(IDX_ERR_INVALID, "x must be 16-byte aligned and x_row_stride a multiple of 8");
+  if (!aligned(w, 4)) return fail(IDX_ERR_INVALID, "w must be 4-byte aligned");
+  idx::QQuantArgs a;
+  a.x = x;
+  a.x_bf16 = x_dtype == IDX_KIN_BF16;
+  a.x_row_stride = x_row_stride;
+  a.R = R;
+  a.dtype = out->dtype;
+  a.w = w;
+  a.c = c;
+  a.q = static_cast<uint8_t *>(const_cast<void *>(out->q));
+  a.q_scale = static_cast<uint8_t *>(const_cast<void *>(out->q_scale));
+  a.w_out = const_cast<float *>(out->weights);
+  hipError_t e = idx::launch_q_quant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "query quantization launch");
   return ok();
 }
 

@@ -101,7 +101,21 @@ struct KvWriteArgs {
   int32_t page_shift; // log2 of the page size
 };
 
+struct QQuantArgs {
+  const void *x;        // [R][64][128] fp32 or bf16
+  int32_t x_bf16;
+  int64_t x_row_stride; // elements between rows
+  int32_t R;
+  int32_t dtype;        // IDX_FP8_E4M3 / IDX_MXFP4
+  const float *w;       // [R][64]
+  float c;              // constant folded into the weights
+  uint8_t *q;           // codes: FP8 [R][8192] / MXFP4 [R][4096]
+  uint8_t *q_scale;     // FP8: fp32 [R] or null (folded); MXFP4: E8M0 [R][256]
+  float *w_out;         // [R][64]
+};
+
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_logits_fp8_decode(const LogitsArgs &a, hipStream_t s);
 hipError_t launch_logits_mxfp4_decode(const LogitsArgs &a, hipStream_t s);

@@ -40,34 +40,6 @@ __device__ inline void load_pair(const KvWriteArgs &a, int64_t i, float &x0, flo
   }
 }
 
-// Nearest E4M3FN code to y (|y| <= 448 up to rounding), ties to the even code.
-__device__ inline uint32_t fp8_e4m3_rne(float y) {
-  const uint32_t b = __float_as_uint(y);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // subnormal range: multiples of 2^-9; rintf rounds half to even
-    code = (uint32_t)rintf(a * 512.0f); // 8 means the smallest normal, 0x08
-  } else {
-    // normal: keep 3 mantissa bits of the fp32 pattern, round half to even
-    const uint32_t ab = __float_as_uint(a);
-    const uint32_t lsb = (ab >> 20) & 1u;
-    const uint32_t r = ab + 0x7FFFFu + lsb;        // may carry into the exponent
-    const uint32_t exp = (r >> 23) - 127 + 7;      // E4M3 biased exponent
-    code = (exp << 3) | ((r >> 20) & 7u);
-    if (code > 0x7Eu) code = 0x7Eu; // saturate at 448
-  }
-  return code | sign;
-}
-
-// Nearest E2M1 magnitude code (0..7) to a >= 0, ties to the even code,
-// saturating at 6.
-__device__ inline uint32_t e2m1_rne(float a) {
-  return (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
-         (a > 5.0f);
-}
-
 // Quantizes one row (x0, x1 = this lane's two values) into its slot.
 __device__ inline void write_row(const KvWriteArgs &a, int64_t slot, float x0, float x1) {
   const int lane = threadIdx.x & 63;
@@ -88,13 +60,7 @@ __device__ inline void write_row(const KvWriteArgs &a, int64_t slot, float x0, f
   } else {
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64)); // 16-lane block
-    int e = 0;
-    if (m > 0.f) {
-      int ex;
-      (void)frexpf(m, &ex); // m = f * 2^ex, f in [0.5, 1)
-      e = ex - 1 - 2;
-      e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    }
+    const int e = mx_block_exponent(m);
     const float y0 = ldexpf(x0, -e), y1 = ldexpf(x1, -e);
     uint32_t c0 = e2m1_rne(fabsf(y0)), c1 = e2m1_rne(fabsf(y1));
     if (y0 < 0.f && c0) c0 |= 8u;

@@ -391,7 +391,7 @@ def to_device(case, device="cuda"):
     c = case.cache
     out = {
         "q": t(case.q),
-        "q_scale": t(case.q_scale),
+        "q_scale": None if case.q_scale is None else t(case.q_scale),
         "w": t(case.w),
         "kdata": t(c.data),
         "kscale": None if c.scale_offset >= 0 else t(c.scale),

@@ -210,3 +210,36 @@ def test_kv_write_of_no_rows_is_a_no_op(lib):
     # N = 0 launches nothing, so it succeeds without touching the (fake) pointers
     assert _kvw(k=0, sm=0, N=0) == idx.IDX_OK
     assert _kvw(k=0x8002, kd=1, N=0) == idx.IDX_OK
+
+
+def _qq(x=0x8000, xd=0, ld=8192, R=4, w=0x9000, c=1.0, out=None, dtype=idx.IDX_FP8_E4M3,
+        qs=0xA000):
+    out = out if out is not None else idx.Query(dtype, 64, 128, 0, 0xB000, qs, 0xC000)
+    return idx.load().idx_quantize_query(x, xd, ld, R, w, c, ctypes.byref(out), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), idx.IDX_ERR_INVALID),
+    (dict(w=0), idx.IDX_ERR_INVALID),
+    (dict(xd=2), idx.IDX_ERR_INVALID),
+    (dict(ld=8191), idx.IDX_ERR_INVALID),
+    (dict(ld=8196), idx.IDX_ERR_INVALID),           # rows read eight values at a time
+    (dict(x=0x8008), idx.IDX_ERR_INVALID),          # x needs 16-byte alignment
+    (dict(w=0x9002), idx.IDX_ERR_INVALID),
+    (dict(R=-1), idx.IDX_ERR_INVALID),
+    (dict(c=float("inf")), idx.IDX_ERR_INVALID),
+    (dict(c=float("nan")), idx.IDX_ERR_INVALID),
+    (dict(dtype=5), idx.IDX_ERR_UNSUPPORTED),
+    (dict(dtype=idx.IDX_MXFP4, qs=0), idx.IDX_ERR_INVALID),  # MXFP4 scales have nowhere to fold
+    (dict(out=idx.Query(1, 32, 128, 0, 0xB000, 0, 0xC000)), idx.IDX_ERR_UNSUPPORTED),
+    (dict(out=idx.Query(1, 64, 128, 0, 0xB008, 0, 0xC000)), idx.IDX_ERR_INVALID),
+    (dict(out=idx.Query(1, 64, 128, 0, 0xB000, 0, 0)), idx.IDX_ERR_INVALID),
+])
+def test_quantize_query_rejects_bad_arguments(lib, kw, status):
+    assert _qq(**kw) == status
+    assert idx.idx_last_error_message() != ""
+
+
+def test_quantize_query_of_no_rows_is_a_no_op(lib):
+    assert _qq(x=0, w=0, R=0) == idx.IDX_OK
+    assert _qq(R=0, out=idx.Query(1, 64, 128, 0, 0, 0, 0)) == idx.IDX_OK

@@ -496,3 +496,100 @@ def test_oracle_kv_write_scatters_and_skips():
         assert np.array_equal(cache.data[~touched], data0[~touched])
         changed_scales = np.nonzero(cache.scale != scale0)[0] // 4
         assert set(changed_scales.tolist()) <= {5, 3 * P + 31, 0, 40}
+
+
+# ------------------------------------------------------ query quantization
+
+def _query_rows(R, seed, H=64, D=128):
+    """Query rows whose heads differ in magnitude by up to 2^12, with exact
+    zeros, a zero head and a zero row mixed in."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, H, D)).astype(np.float32)
+    x *= np.exp2(rng.integers(-6, 7, size=(R, H, 1))).astype(np.float32)
+    x[:, :, ::17] = 0.0
+    if R > 1:
+        x[1, 3] = 0.0
+    if R > 2:
+        x[2] = 0.0
+    return x
+
+
+def test_query_fp8_quantizer_matches_torch_cast_and_folds_the_scale():
+    """FP8 query rows: one fp32 scale per row, amax/448 (numpy single
+    precision; 1 for the zero row); codes equal torch's float8_e4m3fn cast of
+    x/s; folded weights are (w*s)*c and unfolded ones w*c with s returned."""
+    x = _query_rows(5, 41)
+    w = np.random.default_rng(42).standard_normal((5, 64)).astype(np.float32)
+    c = np.float32(0.125 * 0.0883883)
+    q, qs, wf = oracle.quantize_query(oracle.FP8, x, w, c, fold=True)
+    q2, qs2, wu = oracle.quantize_query(oracle.FP8, x, w, c, fold=False)
+    assert qs is None and np.array_equal(q, q2)
+    amax = np.abs(x.reshape(5, -1)).max(axis=1)
+    s = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+    assert s[2] == 1.0 and np.array_equal(qs2, s)
+    want = torch.from_numpy(x / s[:, None, None]).to(torch.float8_e4m3fn)
+    assert np.array_equal(q, want.view(torch.uint8).numpy())
+    assert np.array_equal(wf, (w * s[:, None]) * c)
+    assert np.array_equal(wu, w * c)
+
+
+def test_query_mxfp4_quantizer_is_the_block_quantizer_per_head():
+    """MXFP4 query rows: each head's 128 values carry four E8M0 bytes and
+    their E2M1 codes exactly as the (separately pinned) block quantizer makes
+    them; weights are w*c; dequantized values stay within half an E2M1 step
+    of x (steps 0.5 / 1 / 2 times 2^e below 2 / 4 / 6), or at 6*2^e for
+    |x| in [6, 8)*2^e (saturation; the block maximum is below 8*2^e)."""
+    x = _query_rows(3, 43)
+    w = np.random.default_rng(44).standard_normal((3, 64)).astype(np.float32)
+    q, qs, wo = oracle.quantize_query(oracle.MXFP4, x, w, np.float32(2.0))
+    assert q.shape == (3, 64, 64) and qs.shape == (3, 64, 4)
+    for r in range(3):
+        for h in range(64):
+            p, sc = oracle.quant_mxfp4_row(x[r, h])
+            assert np.array_equal(q[r, h], p) and np.array_equal(qs[r, h], sc)
+    assert np.array_equal(wo, w * np.float32(2.0))
+    nib = np.stack([q & 15, q >> 4], axis=-1).reshape(3, 64, 128)
+    mag = np.array([oracle.dec_e2m1(int(n)) for n in range(16)])[nib]
+    e = qs.astype(np.int64) - 127
+    deq = mag * np.exp2(np.repeat(e, 32, axis=-1))
+    y = np.abs(x) / np.exp2(np.repeat(e, 32, axis=-1))
+    assert np.all(y < 8)
+    ulp = np.exp2(np.repeat(e, 32, axis=-1))
+    allowed = np.where(y < 2, 0.25, np.where(y < 4, 0.5, np.where(y <= 6, 1.0, y - 6))) * ulp
+    assert np.all(np.abs(deq - x) <= allowed * (1 + 1e-6))
+    assert np.all(np.sign(deq) * np.sign(x) >= 0)
+
+
+def test_folded_and_unfolded_queries_score_alike_and_near_the_real_query():
+    """Scoring the folded FP8 query (q_scale dropped, s in the weights) equals
+    scoring the unfolded one up to rounding, because max(0, s*y) = s*max(0, y)
+    for s > 0; both are close to the scores of the unquantized query against
+    the same keys (E4M3 keeps 3 mantissa bits: each q element within 2^-4
+    relative, so each head's dot product within 2^-4 of sum |q_i k_i|)."""
+    case = synth.decode_case([150, 70], next_n=1, P=64, H=64, D=128, k=8, seed=45,
+                             canary=False)
+    x = _query_rows(2, 46)
+    w = case.w.astype(np.float32)
+    c = np.float32(0.5)
+    qf, _, wf = oracle.quantize_query(oracle.FP8, x, w, c, fold=True)
+    qu, su, wu = oracle.quantize_query(oracle.FP8, x, w, c, fold=False)
+    case.q, case.q_scale, case.w = qf, None, wf
+    folded, E = _decode_all(case)
+    case.q, case.q_scale, case.w = qu, su, wu
+    unfolded, _ = _decode_all(case)
+    # the real query against the same dequantized keys, in float64; an E4M3
+    # element is within 2^-4 relative when normal and within 2^-10 * s when
+    # subnormal, and max(0, .) is 1-Lipschitz
+    for r in range(2):
+        n = E[r]
+        assert n > 0
+        keys = _dense_keys_fp8(case, r)
+        scale = np.abs(unfolded[r, :n]).max()
+        assert np.max(np.abs(folded[r, :n] - unfolded[r, :n])) <= 1e-6 * scale
+        x64 = x[r].astype(np.float64)
+        dots = x64 @ keys.T
+        err = np.abs(x64) * 2.0 ** -4 + float(su[r]) * 2.0 ** -10
+        real = (w[r, :, None].astype(np.float64) * c * np.maximum(dots, 0)).sum(axis=0)
+        bound = (np.abs(w[r, :, None]) * c * (err @ np.abs(keys).T)).sum(axis=0)
+        assert np.all(np.abs(unfolded[r, :n] - real) <= bound * (1 + 1e-9) + 1e-12)
+        assert np.max(np.abs(unfolded[r, :n] - real)) <= 0.05 * np.abs(real).max()
