@@ -153,6 +153,48 @@ idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
                                 const int32_t *cta_info, int32_t n_ctas, float *logits,
                                 int64_t W, void *stream);
 
+/*
+ * Ragged decode (speculative decoding with per-sequence draft counts): the
+ * query rows of a step are packed, sequence b owning rows
+ * [row_offsets[b], row_offsets[b+1]) -- n_b = row_offsets[b+1] -
+ * row_offsets[b] rows, 0 <= n_b <= max_q <= 4 -- and its row j sees
+ * E = max(0, context_lens[b] - (n_b - 1 - j)) tokens: each draft row's window
+ * ends at its own position (ATOM PR #1709, commits on the ragged varlen
+ * windows: the windows move every decode step and a rectangular step is the
+ * uniform case n_b = next_n; offsets b*next_n reproduce idx_paged_mqa_logits
+ * exactly). Buffers keep the fixed shape of B*max_q rows so a captured graph
+ * stays valid whatever the step's draft counts are:
+ *   q, weights, q_scale  rows [0, B*max_q); rows >= row_offsets[B] unread
+ *   row_offsets          int32 [B+1], device, non-decreasing from 0, read at
+ *                        kernel time (offsets outside the contract drop rows;
+ *                        they never address outside the B*max_q rows)
+ *   cta_info             idx_build_schedule(context_lens, B, max_q, ...)
+ *   logits               fp32 [B*max_q][W]; only rows < row_offsets[B] and
+ *                        columns < their E are written
+ * Other arguments and errors as idx_paged_mqa_logits (max_q in place of
+ * next_n), plus IDX_ERR_INVALID for a null or misaligned row_offsets. A
+ * sequence with no rows still costs its scan: pass a 0 length for it.
+ */
+idx_status idx_paged_mqa_logits_varlen(const idx_query *q, const idx_kv_cache *kv,
+                                       const int32_t *block_tables, int64_t bt_stride,
+                                       const int32_t *context_lens, const int32_t *row_offsets,
+                                       int32_t B, int32_t max_q, const int32_t *cta_info,
+                                       int32_t n_ctas, float *logits, int64_t W, void *stream);
+
+/*
+ * Per-row visible ends of a ragged decode step, built on the device every
+ * step ("compute_varqlen_windows" in ATOM PR #1709: stale windows replayed
+ * by a captured graph were the cause of a memory fault there). Writes
+ * visible_end[r] for every r < B*max_q: the E of the row's owner as in
+ * idx_paged_mqa_logits_varlen, 0 for rows no sequence owns. Then
+ * idx_topk(logits, W, visible_end, B*max_q, 1, k, ...) selects per packed
+ * row, with empty selections for the unowned rows.
+ * Errors: IDX_ERR_INVALID (null or misaligned pointers, B outside [1, 16000],
+ * max_q outside [1, 4]).
+ */
+idx_status idx_varlen_windows(const int32_t *context_lens, const int32_t *row_offsets, int32_t B,
+                              int32_t max_q, int32_t *visible_end, void *stream);
+
 /* Workspace bytes idx_topk needs for `rows` rows of width W (0 for W <= 65536). */
 size_t idx_topk_workspace_size(int32_t rows, int64_t W, int32_t k);
 

@@ -77,6 +77,11 @@ def _load():
         lib.orc_quantize_query.restype = i32
         lib.orc_quantize_query.argtypes = [i32, P, i64, i64, i32, i32, P, ctypes.c_float, i32,
                                            P, P, P]
+        lib.orc_varlen_windows.restype = i32
+        lib.orc_varlen_windows.argtypes = [P, P, i32, i64, P]
+        lib.orc_varlen_logits.restype = i32
+        lib.orc_varlen_logits.argtypes = [i32, P, P, P, i32, i32, P, i64, i64, P, i64, i64, i32,
+                                          i64, P, i64, P, P, i32, i64, P, i64, i64, P, P]
         _lib = lib
     return _lib
 
@@ -259,3 +264,38 @@ def quantize_query(dtype, x, w, c=1.0, fold=True):
     if rc != 0:
         raise ValueError("oracle quantize_query failed with code %d" % rc)
     return q, qs, w_out
+
+
+def varlen_windows(lens, row_offsets, R):
+    """Visible ends (int64 [R]) of the packed rows of a ragged decode step."""
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    off = np.ascontiguousarray(row_offsets, dtype=np.int32)
+    E = np.empty(R, dtype=np.int64)
+    rc = _load().orc_varlen_windows(_ptr(lens), _ptr(off), len(lens), R, _ptr(E))
+    if rc != 0:
+        raise ValueError("oracle varlen_windows failed with code %d" % rc)
+    return E
+
+
+def varlen_logits(dtype, q, q_scale, w, H, D, cache: Cache, block_tables, lens, row_offsets,
+                  R, rows, W):
+    """Double-precision logits of the listed packed rows of a ragged decode
+    step; returns (logits [len(rows), W], E [len(rows)])."""
+    lib = _load()
+    q = _u8(q)
+    qs = _u8(q_scale)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    off = np.ascontiguousarray(row_offsets, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), W), dtype=np.float64)
+    E = np.empty(len(rows), dtype=np.int64)
+    rc = lib.orc_varlen_logits(
+        dtype, _ptr(q), _ptr(qs), _ptr(w), H, D, _ptr(cache.data), cache.page_stride,
+        cache.row_stride, _ptr(cache.scale), cache.scale_page_stride, cache.scale_row_stride,
+        cache.page_size, cache.num_pages, _ptr(bt), bt.shape[1], _ptr(lens), _ptr(off),
+        len(lens), R, _ptr(rows), len(rows), W, _ptr(out), _ptr(E))
+    if rc != 0:
+        raise ValueError("oracle varlen_logits failed with code %d" % rc)
+    return out, E

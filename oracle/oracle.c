@@ -575,3 +575,95 @@ int orc_quantize_query(int dtype, const float *x, int64_t ld, int64_t R, int H, 
     }
     return ORC_OK;
 }
+
+/* ---- Ragged decode (ATOM PR #1709, commits on the ragged varlen windows:
+ * sequence b's draft rows see windows ending at its committed length; a
+ * rectangular step is the uniform case). Reading: sequence b owns the packed
+ * rows [off[b], off[b+1]) (n_b of them) and its row j sees
+ * max(0, lens[b] - (n_b - 1 - j)) keys, the rectangular rule with next_n
+ * replaced by n_b. */
+
+/* Sequence owning row r, or -1; by a linear walk over the offsets. */
+static int64_t orc_row_owner(const int32_t *off, int B, int64_t r)
+{
+    int b;
+    for (b = 0; b < B; ++b)
+        if (off[b] <= r && r < off[b + 1])
+            return b;
+    return -1;
+}
+
+/* Visible ends of rows [0, R): the rule above; rows no sequence owns get 0. */
+int orc_varlen_windows(const int32_t *lens, const int32_t *off, int B, int64_t R,
+                       int64_t *E_out)
+{
+    int64_t r;
+    int b;
+    for (b = 0; b < B; ++b)
+        if (off[b] < 0 || off[b + 1] < off[b])
+            return ORC_BAD_ARG;
+    for (r = 0; r < R; ++r) {
+        const int64_t o = orc_row_owner(off, B, r);
+        int64_t E = 0;
+        if (o >= 0) {
+            const int64_t n = off[o + 1] - off[o];
+            const int64_t j = r - off[o];
+            E = (int64_t)lens[o] - (n - 1 - j);
+            if (E < 0)
+                E = 0;
+        }
+        E_out[r] = E;
+    }
+    return ORC_OK;
+}
+
+/* Logits of the listed packed rows of a ragged decode step (rows no sequence
+ * owns have E = 0 and an all -inf output). */
+int orc_varlen_logits(int dtype, const uint8_t *q, const uint8_t *q_scale,
+                      const float *w, int H, int D, const uint8_t *kdata,
+                      int64_t page_stride, int64_t row_stride,
+                      const uint8_t *kscale, int64_t scale_page_stride,
+                      int64_t scale_row_stride, int page_size, int64_t num_pages,
+                      const int32_t *block_tables, int64_t bt_stride,
+                      const int32_t *lens, const int32_t *off, int B, int64_t R,
+                      const int64_t *rows, int64_t nrows, int64_t W, double *out,
+                      int64_t *E_out)
+{
+    int64_t i;
+    int rc_all = ORC_OK;
+    int64_t *Eall;
+    if (orc_check_common(dtype, H, D, page_size) != ORC_OK)
+        return ORC_BAD_ARG;
+    for (i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= R)
+            return ORC_BAD_ARG;
+    Eall = (int64_t *)malloc((size_t)(R > 0 ? R : 1) * sizeof(int64_t));
+    if (!Eall)
+        return ORC_BAD_ARG;
+    if (orc_varlen_windows(lens, off, B, R, Eall) != ORC_OK) {
+        free(Eall);
+        return ORC_BAD_ARG;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        const int64_t r = rows[i];
+        const int64_t b = orc_row_owner(off, B, r);
+        int rc;
+        int64_t t;
+        E_out[i] = Eall[r];
+        if (b < 0) {
+            for (t = 0; t < W; ++t)
+                out[i * W + t] = -INFINITY;
+            continue;
+        }
+        rc = orc_row(dtype, q, q_scale, w, H, D, r, kdata, page_stride, row_stride, kscale,
+                     scale_page_stride, scale_row_stride, page_size, num_pages,
+                     block_tables + b * bt_stride, Eall[r], W, out + i * W);
+        if (rc != ORC_OK) {
+#pragma omp critical
+            rc_all = rc;
+        }
+    }
+    free(Eall);
+    return rc_all;
+}

@@ -29,7 +29,8 @@ IDX_KIN_BF16 = 1
 # Every symbol include/idx.h declares.
 EXPORTS = (
     "idx_schedule_ints", "idx_recommended_ctas", "idx_build_schedule",
-    "idx_paged_mqa_logits", "idx_topk_workspace_size", "idx_topk",
+    "idx_paged_mqa_logits", "idx_paged_mqa_logits_varlen", "idx_varlen_windows",
+    "idx_topk_workspace_size", "idx_topk",
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
     "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_kv_cache_write",
     "idx_quantize_query", "idx_status_string", "idx_last_error", "idx_version",
@@ -84,6 +85,9 @@ def load(path: str = LIB_PATH):
         "idx_build_schedule": (st, [P, i32, i32, i32, i32, P, P]),
         "idx_paged_mqa_logits": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P, i64,
                                       P, i32, i32, P, i32, P, i64, P]),
+        "idx_paged_mqa_logits_varlen": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P,
+                                             i64, P, P, i32, i32, P, i32, P, i64, P]),
+        "idx_varlen_windows": (st, [P, P, i32, i32, P, P]),
         "idx_topk_workspace_size": (sz, [i32, i64, i32]),
         "idx_topk": (st, [P, i64, P, i32, i32, i32, P, P, P, sz, P]),
         "idx_prefill_rows_per_chunk": (i64, [i64, i64]),
@@ -224,3 +228,18 @@ def idx_quantize_query(x, x_dtype, x_row_stride, R, w, c, out: Query, stream=Non
     _check(load().idx_quantize_query(ptr(x), x_dtype, x_row_stride, R, ptr(w), c,
                                      ctypes.byref(out), stream_handle(stream)),
            "idx_quantize_query")
+
+
+def idx_paged_mqa_logits_varlen(query: Query, kv: KVCache, block_tables, bt_stride,
+                                context_lens, row_offsets, B, max_q, cta_info, n_ctas, logits,
+                                W, stream=None):
+    _check(load().idx_paged_mqa_logits_varlen(
+        ctypes.byref(query), ctypes.byref(kv), ptr(block_tables), bt_stride, ptr(context_lens),
+        ptr(row_offsets), B, max_q, ptr(cta_info), n_ctas, ptr(logits), W,
+        stream_handle(stream)), "idx_paged_mqa_logits_varlen")
+
+
+def idx_varlen_windows(context_lens, row_offsets, B, max_q, visible_end, stream=None):
+    _check(load().idx_varlen_windows(ptr(context_lens), ptr(row_offsets), B, max_q,
+                                     ptr(visible_end), stream_handle(stream)),
+           "idx_varlen_windows")

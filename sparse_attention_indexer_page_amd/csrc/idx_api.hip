@@ -180,11 +180,13 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
   return ok();
 }
 
-idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
-                                const int32_t *block_tables, int64_t bt_stride,
-                                const int32_t *context_lens, int32_t B, int32_t next_n,
-                                const int32_t *cta_info, int32_t n_ctas, float *logits,
-                                int64_t W, void *stream) {
+namespace {
+
+idx_status decode_logits(const idx_query *q, const idx_kv_cache *kv, const int32_t *block_tables,
+                         int64_t bt_stride, const int32_t *context_lens,
+                         const int32_t *row_offsets, int32_t B, int32_t next_n,
+                         const int32_t *cta_info, int32_t n_ctas, float *logits, int64_t W,
+                         void *stream) {
   idx_status st = check_query(q);
   if (st != IDX_OK) return st;
   if ((st = check_cache(kv, q->dtype)) != IDX_OK) return st;
@@ -204,6 +206,8 @@ idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
   a.lens = context_lens;
   a.nseg = B;
   a.next_n = next_n;
+  a.row_offsets = row_offsets;
+  a.row_cap = B * next_n;
   a.cta_info = cta_info;
   a.n_ctas = n_ctas;
   a.logits = logits;
@@ -212,6 +216,43 @@ idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
   hipError_t e = q->dtype == IDX_FP8_E4M3 ? idx::launch_logits_fp8_decode(a, s)
                                           : idx::launch_logits_mxfp4_decode(a, s);
   if (e != hipSuccess) return hip_fail(e, "logits launch");
+  return ok();
+}
+
+} // namespace
+
+idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
+                                const int32_t *block_tables, int64_t bt_stride,
+                                const int32_t *context_lens, int32_t B, int32_t next_n,
+                                const int32_t *cta_info, int32_t n_ctas, float *logits,
+                                int64_t W, void *stream) {
+  return decode_logits(q, kv, block_tables, bt_stride, context_lens, nullptr, B, next_n,
+                       cta_info, n_ctas, logits, W, stream);
+}
+
+idx_status idx_paged_mqa_logits_varlen(const idx_query *q, const idx_kv_cache *kv,
+                                       const int32_t *block_tables, int64_t bt_stride,
+                                       const int32_t *context_lens, const int32_t *row_offsets,
+                                       int32_t B, int32_t max_q, const int32_t *cta_info,
+                                       int32_t n_ctas, float *logits, int64_t W, void *stream) {
+  if (!row_offsets) return fail(IDX_ERR_INVALID, "row_offsets is null");
+  if (!aligned(row_offsets, 4)) return fail(IDX_ERR_INVALID, "row_offsets misaligned");
+  return decode_logits(q, kv, block_tables, bt_stride, context_lens, row_offsets, B, max_q,
+                       cta_info, n_ctas, logits, W, stream);
+}
+
+idx_status idx_varlen_windows(const int32_t *context_lens, const int32_t *row_offsets, int32_t B,
+                              int32_t max_q, int32_t *visible_end, void *stream) {
+  if (!context_lens || !row_offsets || !visible_end)
+    return fail(IDX_ERR_INVALID, "null context_lens, row_offsets or visible_end");
+  if (B < 1 || B > idx::kMaxSegs)
+    return fail(IDX_ERR_INVALID, "B = %d outside [1, %d]", B, idx::kMaxSegs);
+  if (max_q < 1 || max_q > 4) return fail(IDX_ERR_INVALID, "max_q = %d outside [1, 4]", max_q);
+  if (!aligned(context_lens, 4) || !aligned(row_offsets, 4) || !aligned(visible_end, 4))
+    return fail(IDX_ERR_INVALID, "misaligned int32 arrays");
+  hipError_t e = idx::launch_varlen_windows(context_lens, row_offsets, B, max_q, visible_end,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "windows launch");
   return ok();
 }
 

@@ -63,7 +63,9 @@ struct LogitsArgs {
   int64_t bt_cols;             // readable entries per block-table row
   const int32_t *lens;         // decode context_lens [B]; prefill visible_end [T]
   int32_t nseg;                // decode B; prefill segments of the chunk
-  int32_t next_n;              // decode rows per sequence
+  int32_t next_n;              // decode rows per sequence (the most, with row_offsets)
+  const int32_t *row_offsets;  // decode varlen: sequence s owns rows [off[s], off[s+1]); or null
+  int32_t row_cap;             // decode varlen: rows the query and logits buffers hold
   int32_t row0;                // prefill: first row of the chunk
   int32_t row_end;             // prefill: end row of the chunk
   const int32_t *cta_info;
@@ -116,6 +118,8 @@ struct QQuantArgs {
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t s);
+hipError_t launch_varlen_windows(const int32_t *lens, const int32_t *row_offsets, int32_t B,
+                                 int32_t max_q, int32_t *visible_end, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_logits_fp8_decode(const LogitsArgs &a, hipStream_t s);
 hipError_t launch_logits_mxfp4_decode(const LogitsArgs &a, hipStream_t s);

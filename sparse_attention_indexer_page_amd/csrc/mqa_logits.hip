@@ -101,22 +101,33 @@ __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
-// Rows, visible lengths and output rows of sequence s (its next_n query
-// rows; row j sees the first len - (next_n - 1 - j) keys); returns its length.
+// Rows, visible lengths and output rows of sequence s: its n query rows
+// (next_n, or off[s+1] - off[s] with row offsets), row j seeing the first
+// len - (n - 1 - j) keys; the remaining register rows are padding (-1).
+// Returns the segment's length. With row offsets the count is clamped to
+// [0, next_n] and rows outside [0, row_cap) become padding, so malformed
+// offsets can only drop rows, never address outside the buffers.
 template <int NROW>
 __device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows, int32_t *E,
                                        int32_t *out_rows) {
   const int32_t len = uniform_load(a.lens + s);
+  int32_t base = s * a.next_n, n = a.next_n;
+  if (a.row_offsets != nullptr) {
+    base = uniform_load(a.row_offsets + s);
+    n = uniform_load(a.row_offsets + s + 1) - base;
+    n = n < 0 ? 0 : (n > NROW ? NROW : n);
+  }
   int32_t L = 0;
 #pragma unroll
   for (int i = 0; i < NROW; ++i) {
-    const int r = s * a.next_n + i;
-    int32_t e = len - (a.next_n - 1 - i);
+    const int r = base + i;
+    int32_t e = len - (n - 1 - i);
     e = e > 0 ? e : 0;
-    rows[i] = r;
-    E[i] = e;
-    out_rows[i] = r;
-    L = e > L ? e : L;
+    const bool live = i < n && r >= 0 && (a.row_offsets == nullptr || r < a.row_cap);
+    rows[i] = live ? r : -1;
+    E[i] = live ? e : 0;
+    out_rows[i] = live ? r : -1;
+    L = live && e > L ? e : L;
   }
   return L;
 }

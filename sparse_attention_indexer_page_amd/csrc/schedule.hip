@@ -118,7 +118,54 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
   }
 }
 
+// Per-row visible ends of a ragged decode step (ROCm/ATOM PR #1709, commits
+// on the ragged varlen windows: each sequence's draft rows see a window that
+// ends at its committed length and moves every step, so it is rebuilt on the
+// device each step; a rectangular step is the uniform case). Sequence b owns
+// rows [off[b], off[b+1]), at most max_q of them; its row j sees
+// len_b - (n_b - 1 - j) keys. Every row of the [B * max_q] buffer is written:
+// rows no sequence owns get 0, so a fixed-shape top-k over the whole buffer
+// selects nothing for them.
+__global__ __launch_bounds__(256) void varlen_windows_kernel(const int32_t *lens,
+                                                             const int32_t *off, int32_t B,
+                                                             int32_t max_q, int32_t *ve) {
+  const int64_t rows = (int64_t)B * max_q;
+  for (int64_t r = blockIdx.x * 256ll + threadIdx.x; r < rows; r += (int64_t)gridDim.x * 256) {
+    // last sequence b with off[b] <= r (offsets are non-decreasing)
+    int lo = 0, hi = B;
+    if (off[0] > r) {
+      ve[r] = 0;
+      continue;
+    }
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    const int32_t base = off[lo];
+    int32_t n = off[lo + 1] - base;
+    n = n < 0 ? 0 : (n > max_q ? max_q : n);
+    const int32_t j = (int32_t)(r - base);
+    int32_t e = 0;
+    if (j < n) {
+      const int32_t len = lens[lo] > 0 ? lens[lo] : 0;
+      e = len - (n - 1 - j);
+      e = e > 0 ? e : 0;
+    }
+    ve[r] = e;
+  }
+}
+
 } // namespace
+
+hipError_t launch_varlen_windows(const int32_t *lens, const int32_t *row_offsets, int32_t B,
+                                 int32_t max_q, int32_t *visible_end, hipStream_t s) {
+  const int64_t rows = (int64_t)B * max_q;
+  const int64_t g = (rows + 255) / 256;
+  hipLaunchKernelGGL(varlen_windows_kernel, dim3(g < 1024 ? (unsigned)g : 1024u), dim3(256), 0,
+                     s, lens, row_offsets, B, max_q, visible_end);
+  return hipGetLastError();
+}
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
   const size_t lds = sizeof(int32_t) * (size_t)(a.nseg > 0 ? a.nseg : 1);

@@ -404,3 +404,17 @@ def to_device(case, device="cuda"):
         out["block_table"] = t(case.block_table)
         out["visible_end"] = t(case.visible_end)
     return out
+
+
+def ragged_offsets(rng, B, max_q, forced=(0, 1)):
+    """Row offsets [B+1] of a ragged decode step: sequence b gets n_b query
+    rows drawn from [0, max_q] (the first entries of `forced` and max_q are
+    always present when B allows), packed in order."""
+    n = rng.integers(0, max_q + 1, size=B)
+    for i, v in enumerate(tuple(forced) + (max_q,)):
+        if i < B:
+            n[i] = min(v, max_q)
+    rng.shuffle(n)
+    off = np.zeros(B + 1, dtype=np.int32)
+    off[1:] = np.cumsum(n)
+    return off

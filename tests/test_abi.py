@@ -243,3 +243,25 @@ def test_quantize_query_rejects_bad_arguments(lib, kw, status):
 def test_quantize_query_of_no_rows_is_a_no_op(lib):
     assert _qq(x=0, w=0, R=0) == idx.IDX_OK
     assert _qq(R=0, out=idx.Query(1, 64, 128, 0, 0, 0, 0)) == idx.IDX_OK
+
+
+def test_varlen_entry_points_reject_bad_arguments(lib):
+    q, kv = _q(), _kv()
+    L = idx.load()
+    # row_offsets null / misaligned
+    assert L.idx_paged_mqa_logits_varlen(ctypes.byref(q), ctypes.byref(kv), 0x4000, 8, 0x5000, 0,
+                                         2, 2, 0x6000, 4, 0x7000, 512, None) == idx.IDX_ERR_INVALID
+    assert L.idx_paged_mqa_logits_varlen(ctypes.byref(q), ctypes.byref(kv), 0x4000, 8, 0x5000,
+                                         0x8002, 2, 2, 0x6000, 4, 0x7000, 512,
+                                         None) == idx.IDX_ERR_INVALID
+    # max_q outside [1, 4]
+    assert L.idx_paged_mqa_logits_varlen(ctypes.byref(q), ctypes.byref(kv), 0x4000, 8, 0x5000,
+                                         0x8000, 2, 5, 0x6000, 4, 0x7000, 512,
+                                         None) == idx.IDX_ERR_INVALID
+    assert L.idx_varlen_windows(0x5000, 0x8000, 2, 0, 0x9000, None) == idx.IDX_ERR_INVALID
+    assert L.idx_varlen_windows(0x5000, 0x8000, 2, 5, 0x9000, None) == idx.IDX_ERR_INVALID
+    assert L.idx_varlen_windows(0, 0x8000, 2, 2, 0x9000, None) == idx.IDX_ERR_INVALID
+    assert L.idx_varlen_windows(0x5000, 0x8000, 0, 2, 0x9000, None) == idx.IDX_ERR_INVALID
+    assert L.idx_varlen_windows(0x5000, 0x8000, 16001, 2, 0x9000, None) == idx.IDX_ERR_INVALID
+    assert L.idx_varlen_windows(0x5002, 0x8000, 2, 2, 0x9000, None) == idx.IDX_ERR_INVALID
+    assert idx.idx_last_error_message() != ""

@@ -593,3 +593,56 @@ def test_folded_and_unfolded_queries_score_alike_and_near_the_real_query():
         bound = (np.abs(w[r, :, None]) * c * (err @ np.abs(keys).T)).sum(axis=0)
         assert np.all(np.abs(unfolded[r, :n] - real) <= bound * (1 + 1e-9) + 1e-12)
         assert np.max(np.abs(unfolded[r, :n] - real)) <= 0.05 * np.abs(real).max()
+
+
+# ------------------------------------------------------------ ragged decode
+
+def test_varlen_windows_worked_example():
+    """Sequences of lengths 10, 5, 0, 7, 2 owning 2, 1, 0, 4, 1 packed rows of a
+    12-row buffer: each sequence's last row sees its whole length and each
+    earlier draft row one key less (10: 9, 10; 5: 5; 7: 4, 5, 6, 7; 2: 2); the
+    four rows nobody owns see nothing."""
+    E = oracle.varlen_windows([10, 5, 0, 7, 2], [0, 2, 3, 3, 7, 8], 12)
+    assert E.tolist() == [9, 10, 5, 4, 5, 6, 7, 2, 0, 0, 0, 0]
+
+
+def test_varlen_with_rectangular_offsets_is_the_mtp_rule():
+    """Offsets b*n give the rectangular step: the same windows and the same
+    logits, bit for bit, as the next_n rule."""
+    case = synth.decode_case([0, 1, 3, 64, 100], next_n=3, P=32, H=8, D=128, k=8, seed=47,
+                             canary=False)
+    off = (np.arange(case.B + 1) * 3).astype(np.int32)
+    rect, E = _decode_all(case)
+    assert np.array_equal(oracle.varlen_windows(case.lens, off, case.R), E)
+    got, E2 = oracle.varlen_logits(case.dtype, case.q, case.q_scale, case.w, case.H, case.D,
+                                   _cache(case), case.block_tables, case.lens, off, case.R,
+                                   np.arange(case.R), case.W)
+    assert np.array_equal(E2, E)
+    assert np.array_equal(got, rect)
+
+
+def test_varlen_rows_match_dense_formulation():
+    """Packed ragged rows (0 to 4 per sequence) against a dense numpy
+    relu(Q K^T) w over each owner's gathered keys; unowned rows see nothing."""
+    case = synth.decode_case([50, 0, 130, 7, 64, 1], next_n=4, P=32, H=16, D=128, k=8, seed=48,
+                             canary=False)
+    off = synth.ragged_offsets(np.random.default_rng(49), case.B, 4)
+    got, E = oracle.varlen_logits(case.dtype, case.q, case.q_scale, case.w, case.H, case.D,
+                                  _cache(case), case.block_tables, case.lens, off, case.R,
+                                  np.arange(case.R), case.W)
+    owner = np.full(case.R, -1)
+    for b in range(case.B):
+        owner[off[b]:off[b + 1]] = b
+    assert np.all(E[owner < 0] == 0) and np.all(np.isneginf(got[owner < 0]))
+    for r in np.nonzero(owner >= 0)[0]:
+        b = owner[r]
+        n, j = off[b + 1] - off[b], r - off[b]
+        e = int(E[r])
+        assert e == max(0, int(case.lens[b]) - (n - 1 - j))
+        kf = _dense_keys_fp8(case, b)[:e]
+        qf = torch.from_numpy(case.q[r].copy()).view(torch.float8_e4m3fn).double().numpy()
+        qf = qf * float(case.q_scale[r])
+        ref = (np.maximum(qf @ kf.T, 0.0) * case.w[r].astype(np.float64)[:, None]).sum(axis=0)
+        scale = max(np.abs(ref).max() if e else 1.0, 1e-30)
+        assert np.max(np.abs(got[r, :e] - ref), initial=0.0) <= 1e-12 * scale
+        assert np.all(np.isneginf(got[r, e:]))
