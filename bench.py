@@ -283,7 +283,7 @@ def prefill_bench(args, torch, idx, synth):
 
     def call():
         idx.idx_prefill_chunked_topk(query, kv, dev["block_table"], dev["visible_end"], T, W,
-                                     case.budget_bytes, k, scratch, sb, cta, si, out)
+                                     case.budget_bytes, k, 0, scratch, sb, cta, si, out)
 
     for _ in range(2):
         call()

@@ -242,7 +242,13 @@ int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes);
  *                  right-sized width max_r visible_end[r])
  *   logits_scratch fp32, scratch_bytes >= idx_prefill_scratch_bytes(T, W, budget)
  *   cta_scratch    int32, cta_scratch_ints >= idx_prefill_schedule_ints(...)
- *   out_idx        int32 [T][k], seq-local indices as in idx_topk
+ *   index_base     host, >= 0: added to every selected index (padding stays
+ *                  -1). 0 gives sequence-local indices (the FP4 path's output
+ *                  in ATOM PR #1709); the sequence's first token in the
+ *                  batch's flattened key order gives the GLOBAL indices of
+ *                  that page's FP8 prefill path. index_base + W < 2^31.
+ *   out_idx        int32 [T][k], ascending indices as in idx_topk, plus
+ *                  index_base
  * The host loop over chunks enqueues schedule, scores and top-k per chunk on
  * `stream` without synchronizing.
  * Errors: as idx_paged_mqa_logits and idx_topk; IDX_ERR_WORKSPACE when a
@@ -251,9 +257,9 @@ int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes);
 idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
                                     const int32_t *block_table, const int32_t *visible_end,
                                     int32_t T, int64_t W, int64_t budget_bytes, int32_t k,
-                                    float *logits_scratch, int64_t scratch_bytes,
-                                    int32_t *cta_scratch, int64_t cta_scratch_ints,
-                                    int32_t *out_idx, void *stream);
+                                    int32_t index_base, float *logits_scratch,
+                                    int64_t scratch_bytes, int32_t *cta_scratch,
+                                    int64_t cta_scratch_ints, int32_t *out_idx, void *stream);
 
 /* Element type of the rows idx_kv_cache_write and idx_quantize_query
  * quantize. */

@@ -94,7 +94,7 @@ def load(path: str = LIB_PATH):
         "idx_prefill_scratch_bytes": (i64, [i32, i64, i64]),
         "idx_prefill_schedule_ints": (i64, [i32, i64, i64]),
         "idx_prefill_chunked_topk": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P, P,
-                                          i32, i64, i64, i32, P, i64, P, i64, P, P]),
+                                          i32, i64, i64, i32, i32, P, i64, P, i64, P, P]),
         "idx_kv_cache_write": (st, [P, i32, i64, i32, P, ctypes.POINTER(KVCache), P]),
         "idx_quantize_query": (st, [P, i32, i64, i32, P, ctypes.c_float,
                                     ctypes.POINTER(Query), P]),
@@ -203,11 +203,12 @@ def idx_prefill_schedule_ints(T, W, budget_bytes) -> int:
 
 
 def idx_prefill_chunked_topk(query: Query, kv: KVCache, block_table, visible_end, T, W,
-                             budget_bytes, k, logits_scratch, scratch_bytes, cta_scratch,
-                             cta_scratch_ints, out_idx, stream=None):
+                             budget_bytes, k, index_base, logits_scratch, scratch_bytes,
+                             cta_scratch, cta_scratch_ints, out_idx, stream=None):
     _check(load().idx_prefill_chunked_topk(ctypes.byref(query), ctypes.byref(kv),
                                            ptr(block_table), ptr(visible_end), T, W,
-                                           budget_bytes, k, ptr(logits_scratch), scratch_bytes,
+                                           budget_bytes, k, index_base, ptr(logits_scratch),
+                                           scratch_bytes,
                                            ptr(cta_scratch), cta_scratch_ints, ptr(out_idx),
                                            stream_handle(stream)),
            "idx_prefill_chunked_topk")

@@ -288,6 +288,7 @@ idx_status idx_topk(const float *logits, int64_t W, const int32_t *context_lens,
   a.k = k;
   a.out_idx = out_idx;
   a.out_count = out_count;
+  a.index_base = 0;
   hipError_t e = idx::launch_topk(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
@@ -392,9 +393,9 @@ int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes) {
 idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
                                     const int32_t *block_table, const int32_t *visible_end,
                                     int32_t T, int64_t W, int64_t budget_bytes, int32_t k,
-                                    float *logits_scratch, int64_t scratch_bytes,
-                                    int32_t *cta_scratch, int64_t cta_scratch_ints,
-                                    int32_t *out_idx, void *stream) {
+                                    int32_t index_base, float *logits_scratch,
+                                    int64_t scratch_bytes, int32_t *cta_scratch,
+                                    int64_t cta_scratch_ints, int32_t *out_idx, void *stream) {
   idx_status st = check_query(q);
   if (st != IDX_OK) return st;
   if ((st = check_cache(kv, q->dtype)) != IDX_OK) return st;
@@ -407,6 +408,9 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
                 idx::kTopkMaxW);
   if (k < 1) return fail(IDX_ERR_INVALID, "k = %d must be >= 1", k);
   if (budget_bytes < 1) return fail(IDX_ERR_INVALID, "budget_bytes must be >= 1");
+  if (index_base < 0 || (int64_t)index_base + W > (1ll << 31) - 1)
+    return fail(IDX_ERR_INVALID, "index_base %d must be >= 0 with index_base + W < 2^31",
+                index_base);
   const int64_t rows = prefill_chunk_rows(T, W, budget_bytes);
   if (scratch_bytes < 4 * W * rows)
     return fail(IDX_ERR_WORKSPACE, "logits scratch %lld B < %lld B", (long long)scratch_bytes,
@@ -457,6 +461,7 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
     ta.k = k;
     ta.out_idx = out_idx + r0 * k;
     ta.out_count = nullptr;
+    ta.index_base = index_base;
     e = idx::launch_topk(ta, s);
     if (e != hipSuccess) return hip_fail(e, "prefill top-k launch");
   }

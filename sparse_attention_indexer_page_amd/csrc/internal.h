@@ -84,6 +84,7 @@ struct TopkArgs {
   int32_t k;
   int32_t *out_idx;   // [R][k]
   int32_t *out_count; // [R] or null
+  int32_t index_base;  // added to every selected index (0: sequence-local)
 };
 
 struct KvWriteArgs {

@@ -161,7 +161,7 @@ __device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint
 // Selects the top k of a row of E > k scores, IPT keys per lane.
 template <int NT, int IPT>
 __device__ __forceinline__ void select_row(const float *row, int E, int k, int32_t *out,
-                                           TopkShared &sm) {
+                                           int32_t ib, TopkShared &sm) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -419,7 +419,7 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
       const bool sel = key[i] >= thr_ge;
       const uint64_t msel = __ballot(sel);
       const int p = pos + lanes_below(msel);
-      if (sel && p < k) out[p] = base + i * 64 + lane;
+      if (sel && p < k) out[p] = ib + base + i * 64 + lane;
       pos += (int)__popcll(msel);
     }
   } else {
@@ -432,7 +432,7 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
       const bool sel = key[i] > thr || (eq && eq_seen + lanes_below(meq) < need_eq);
       const uint64_t msel = __ballot(sel);
       const int p = pos + lanes_below(msel);
-      if (sel && p < k) out[p] = base + i * 64 + lane;
+      if (sel && p < k) out[p] = ib + base + i * 64 + lane;
       pos += (int)__popcll(msel);
       eq_seen += (int)__popcll(meq);
     }
@@ -456,16 +456,19 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   if (a.out_count && tid == 0) a.out_count[r] = E < k ? E : k;
 
   if (E <= k) { // everything visible is selected
-    for (int i = tid; i < k; i += NT) out[i] = i < E ? i : -1;
+    for (int i = tid; i < k; i += NT) out[i] = i < E ? a.index_base + i : -1;
     return;
   }
   const float *row = a.logits + (int64_t)r * a.W;
   // the smallest bucket of keys per lane that holds the row
-  if (E <= NT * 4) select_row<NT, 4>(row, E, k, out, sm);
-  else if (MAXIPT >= 8 && E <= NT * 8) select_row<NT, (MAXIPT >= 8 ? 8 : 4)>(row, E, k, out, sm);
-  else if (MAXIPT >= 16 && E <= NT * 16) select_row<NT, (MAXIPT >= 16 ? 16 : 4)>(row, E, k, out, sm);
-  else if (MAXIPT >= 32 && E <= NT * 32) select_row<NT, (MAXIPT >= 32 ? 32 : 4)>(row, E, k, out, sm);
-  else if (MAXIPT >= 64) select_row<NT, (MAXIPT >= 64 ? 64 : 4)>(row, E, k, out, sm);
+  const int32_t ib = a.index_base;
+  if (E <= NT * 4) select_row<NT, 4>(row, E, k, out, ib, sm);
+  else if (MAXIPT >= 8 && E <= NT * 8) select_row<NT, (MAXIPT >= 8 ? 8 : 4)>(row, E, k, out, ib, sm);
+  else if (MAXIPT >= 16 && E <= NT * 16)
+    select_row<NT, (MAXIPT >= 16 ? 16 : 4)>(row, E, k, out, ib, sm);
+  else if (MAXIPT >= 32 && E <= NT * 32)
+    select_row<NT, (MAXIPT >= 32 ? 32 : 4)>(row, E, k, out, ib, sm);
+  else if (MAXIPT >= 64) select_row<NT, (MAXIPT >= 64 ? 64 : 4)>(row, E, k, out, ib, sm);
 }
 
 // ---- one wave per row, for widths up to 4096 --------------------------------
@@ -558,7 +561,7 @@ __device__ __forceinline__ void wave_radix_pass(WaveShared &sm, const uint32_t (
 
 template <int IPT>
 __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, int32_t *out,
-                                                WaveShared &sm) {
+                                                int32_t ib, WaveShared &sm) {
   const int lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(row), (short)0, E * 4, 0x00020000);
@@ -695,7 +698,7 @@ __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, 
     }
     const uint64_t msel = __ballot(sel);
     const int p = pos + lanes_below(msel);
-    if (sel && p < k) out[p] = 64 * i + lane;
+    if (sel && p < k) out[p] = ib + 64 * i + lane;
     pos += (int)__popcll(msel);
   }
 }
@@ -716,13 +719,13 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void topk_wave_kernel(TopkArgs 
   int32_t *out = a.out_idx + (int64_t)r * k;
   if (a.out_count && lane == 0) a.out_count[r] = E < k ? E : k;
   if (E <= k) {
-    for (int i = lane; i < k; i += 64) out[i] = i < E ? i : -1;
+    for (int i = lane; i < k; i += 64) out[i] = i < E ? a.index_base + i : -1;
     return;
   }
   const float *row = a.logits + (int64_t)r * a.W;
-  if (E <= 1024) select_row_wave<16>(row, E, k, out, sm[wave]);
-  else if (E <= 2048) select_row_wave<32>(row, E, k, out, sm[wave]);
-  else select_row_wave<64>(row, E, k, out, sm[wave]);
+  if (E <= 1024) select_row_wave<16>(row, E, k, out, a.index_base, sm[wave]);
+  else if (E <= 2048) select_row_wave<32>(row, E, k, out, a.index_base, sm[wave]);
+  else select_row_wave<64>(row, E, k, out, a.index_base, sm[wave]);
 }
 
 template <int NT, int MAXIPT> hipError_t launch_rows(const TopkArgs &a, hipStream_t s) {

@@ -74,7 +74,7 @@ def run_decode(dc: DeviceCase, n_ctas=None, fill=float("nan"), k=None, stream=No
     return logits.cpu(), out.cpu(), cnt.cpu()
 
 
-def run_prefill(dc: DeviceCase, budget=None, k=None):
+def run_prefill(dc: DeviceCase, budget=None, k=None, index_base=0):
     """Chunked prefill; returns (last chunk's logits scratch, idx) on the CPU."""
     case = dc.case
     k = k or case.k
@@ -87,7 +87,7 @@ def run_prefill(dc: DeviceCase, budget=None, k=None):
     cta = torch.empty(si, dtype=torch.int32, device=dev)
     out = torch.empty((T, k), dtype=torch.int32, device=dev)
     idx.idx_prefill_chunked_topk(dc.query, dc.kv, dc.t["block_table"], dc.t["visible_end"], T, W,
-                                 budget, k, scratch, sb, cta, si, out)
+                                 budget, k, index_base, scratch, sb, cta, si, out)
     torch.cuda.synchronize()
     return scratch.cpu(), out.cpu()
 

@@ -174,11 +174,20 @@ def test_prefill_chunk_rule_reproduces_the_pages_buffer_sizes():
 def test_prefill_rejects_small_scratch(lib):
     q, kv = _q(), _kv()
     rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
-                                      1 << 20, 16, 0x300, 16, 0x400, 1 << 20, 0x500, None)
+                                      1 << 20, 16, 0, 0x300, 16, 0x400, 1 << 20, 0x500, None)
     assert rc == idx.IDX_ERR_WORKSPACE
     rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
-                                      1 << 20, 16, 0x300, 1 << 30, 0x400, 2, 0x500, None)
+                                      1 << 20, 16, 0, 0x300, 1 << 30, 0x400, 2, 0x500, None)
     assert rc == idx.IDX_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("base", [-1, (1 << 31) - 256])
+def test_prefill_rejects_bad_index_base(lib, base):
+    q, kv = _q(), _kv()
+    rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
+                                      1 << 20, 16, base, 0x300, 1 << 30, 0x400, 1 << 20, 0x500,
+                                      None)
+    assert rc == idx.IDX_ERR_INVALID
 
 
 def _kvw(k=0x8000, kd=0, ld=128, N=4, sm=0x9000, kv=None):

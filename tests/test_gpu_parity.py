@@ -224,3 +224,23 @@ def test_prefill_small_matches_oracle_and_is_chunk_invariant(dtype):
     for budget in (4 * case.W * 100, 4 * case.W * 7, 4 * case.W, 1):
         _, o2 = run_prefill(dc, budget=budget)
         assert torch.equal(o2, out), "budget %d changed the selection" % budget
+    # GLOBAL output: the same selection shifted by the sequence's first token
+    # in the batch's key order (padding stays -1), in both top-k kernels
+    for budget in (full_budget, 4 * case.W * 7):
+        _, og = run_prefill(dc, budget=budget, index_base=1_000_003)
+        want = torch.where(out >= 0, out + 1_000_003, out)
+        assert torch.equal(og, want), "index_base at budget %d" % budget
+
+
+def test_prefill_global_indices_in_the_one_wave_top_k():
+    """2100 rows of width 300: the chunk's top-k runs one wave per row; the
+    GLOBAL selection is the local one shifted by index_base."""
+    log("prefill global indices, wave top-k")
+    T = 2100
+    ve = np.minimum(np.arange(T) // 7 + 1, 300)
+    case = synth.prefill_case(T, 300, visible_end=ve, P=64, k=40, W=300, seed=950)
+    dc = DeviceCase(case)
+    _, out = run_prefill(dc, budget=4 * case.W * T)
+    _, og = run_prefill(dc, budget=4 * case.W * T, index_base=77)
+    assert torch.equal(og, torch.where(out >= 0, out + 77, out))
+    assert int((out >= 0).sum(dim=1).min()) == 1  # row 0 sees one token
