@@ -66,9 +66,12 @@ def traffic_from_profile(digest, launch_bytes_key):
     return prof.get(launch_bytes_key)
 
 
-def decode_bench(args, torch, idx, synth, wl=2):
+def decode_bench(args, torch, idx, synth, wl=2, split=None):
     case = synth.workload(wl, canary=False)
     R, W, k, B = case.R, case.W, case.k, case.B
+    split = split or args.split
+    if split == "auto":
+        split = "in-kernel" if B <= 1024 else "buffer"
     c = case.cache
     log("workload %d: B=%d, sum(len)=%d, pool=%d pages" % (wl, B, int(case.lens.sum()), c.num_pages))
     dev = synth.to_device(case)
@@ -86,12 +89,17 @@ def decode_bench(args, torch, idx, synth, wl=2):
     cnt = torch.empty(R, dtype=torch.int32, device="cuda")
     bt_stride = case.block_tables.shape[1]
 
+    # "buffer": the schedule builder writes the split, the scores read it;
+    # "in-kernel": no buffer, each scoring work group computes its own range
+    cta_arg = cta if split == "buffer" else None
+
     def schedule():
-        idx.idx_build_schedule(dev["lens"], B, case.next_n, c.page_size, n_ctas, cta)
+        if split == "buffer":
+            idx.idx_build_schedule(dev["lens"], B, case.next_n, c.page_size, n_ctas, cta)
 
     def scores(kv):
         idx.idx_paged_mqa_logits(query, kv, dev["block_tables"], bt_stride, dev["lens"], B,
-                                 case.next_n, cta, n_ctas, logits, W)
+                                 case.next_n, cta_arg, n_ctas, logits, W)
 
     def topk():
         idx.idx_topk(logits, W, dev["lens"], B, case.next_n, k, out, cnt)
@@ -167,6 +175,7 @@ def decode_bench(args, torch, idx, synth, wl=2):
         "achieved_gbs": achieved,
         "traffic": traffic,
         "n_ctas": n_ctas,
+        "split": split,
         "digest": digest,
         "case": case,
     }
@@ -417,6 +426,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ctas", type=int, default=0, help="schedule work groups (0: recommended)")
     ap.add_argument("--pool-copies", type=int, default=4)
+    ap.add_argument("--split", choices=("auto", "buffer", "in-kernel"), default="auto",
+                    help="decode work split: schedule buffer or computed in the scoring kernel "
+                         "(auto: in-kernel for B <= 1024)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
@@ -451,8 +463,13 @@ def main():
         counter_run(args, torch, idx, synth)
         return
     d = decode_bench(args, torch, idx, synth)
-    log("decode: step %.3f ms, scoring kernel %.3f ms avg (%.3f min), %.0f GB/s" % (
-        d["step_ms"], d["kern_avg_ms"], d["kern_min_ms"], d["achieved_gbs"]))
+    log("decode (%s split): step %.3f ms, scoring kernel %.3f ms avg (%.3f min), %.0f GB/s" % (
+        d["split"], d["step_ms"], d["kern_avg_ms"], d["kern_min_ms"], d["achieved_gbs"]))
+    alt = None
+    if d["split"] == "in-kernel" and not args.no_prefill:
+        alt = decode_bench(args, torch, idx, synth, split="buffer")
+        log("decode (buffer split): step %.3f ms, scoring kernel %.3f ms avg" % (
+            alt["step_ms"], alt["kern_avg_ms"]))
     pre = None if args.no_prefill else prefill_bench(args, torch, idx, synth)
     if pre:
         log("prefill: %.3f ms per chunked call, %.1f TFLOP/s whole call" % (
@@ -503,6 +520,7 @@ def main():
             "seq_len": "U[1024,32768]",
             "parallelism": "single GPU",
             "n_ctas": d["n_ctas"],
+            "split": d["split"],
         },
         "roofline": {
             "bound": "hbm",
@@ -526,6 +544,10 @@ def main():
             "fp8_tflops_whole_call": pre["tflops_whole_call"],
             "fp8_mfma_frac_whole_call": pre["tflops_whole_call"] / FP8_MFMA_PEAK_TFLOPS,
         }
+    if alt:
+        line["decode_with_schedule_buffer"] = {
+            "ms_per_step": alt["step_ms"], "scoring_kernel_us": alt["kern_avg_ms"] * 1e3,
+            "tokens_per_s": alt["tokens"] / (alt["step_ms"] * 1e-3)}
     if kvw:
         line["kv_cache_write"] = kvw
     if qq:

@@ -142,10 +142,15 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
  *                  of tokens [i*P, (i+1)*P); only entries < ceil(len_b / P)
  *                  are read
  *   cta_info       schedule from idx_build_schedule with the same lens, B,
- *                  next_n, page_size and n_ctas (required)
+ *                  next_n, page_size and n_ctas; or NULL when B <= 1024: each
+ *                  work group then computes its own range of the same split
+ *                  from context_lens (the kernel's internal schedule build,
+ *                  which ATOM PR #1709 says a passed cta_info skips), saving
+ *                  the builder launch
  *   logits         fp32 [B*next_n][W]
- * Errors: IDX_ERR_INVALID (null pointer, shape, alignment, W < 1),
- * IDX_ERR_UNSUPPORTED (H != 64, D != 128, dtype mismatch).
+ * Errors: IDX_ERR_INVALID (null pointer, shape, alignment, W < 1, cta_info
+ * NULL with B > 1024), IDX_ERR_UNSUPPORTED (H != 64, D != 128, dtype
+ * mismatch).
  */
 idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
                                 const int32_t *block_tables, int64_t bt_stride,
@@ -168,7 +173,8 @@ idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
  *   row_offsets          int32 [B+1], device, non-decreasing from 0, read at
  *                        kernel time (offsets outside the contract drop rows;
  *                        they never address outside the B*max_q rows)
- *   cta_info             idx_build_schedule(context_lens, B, max_q, ...)
+ *   cta_info             idx_build_schedule(context_lens, B, max_q, ...), or
+ *                        NULL when B <= 1024
  *   logits               fp32 [B*max_q][W]; only rows < row_offsets[B] and
  *                        columns < their E are written
  * Other arguments and errors as idx_paged_mqa_logits (max_q in place of

@@ -190,10 +190,13 @@ idx_status decode_logits(const idx_query *q, const idx_kv_cache *kv, const int32
   idx_status st = check_query(q);
   if (st != IDX_OK) return st;
   if ((st = check_cache(kv, q->dtype)) != IDX_OK) return st;
-  if (!block_tables || !context_lens || !cta_info || !logits)
-    return fail(IDX_ERR_INVALID, "null block_tables, context_lens, cta_info or logits");
+  if (!block_tables || !context_lens || !logits)
+    return fail(IDX_ERR_INVALID, "null block_tables, context_lens or logits");
   if (B < 1 || B > idx::kMaxSegs)
     return fail(IDX_ERR_INVALID, "B = %d outside [1, %d]", B, idx::kMaxSegs);
+  if (!cta_info && B > idx::kInlineSplitMaxSegs)
+    return fail(IDX_ERR_INVALID, "without cta_info B = %d must be <= %d", B,
+                idx::kInlineSplitMaxSegs);
   if (next_n < 1 || next_n > 4) return fail(IDX_ERR_INVALID, "next_n = %d outside [1, 4]", next_n);
   if (bt_stride < 1) return fail(IDX_ERR_INVALID, "bt_stride must be >= 1");
   if (n_ctas < 1 || n_ctas > kMaxCtas)

@@ -12,6 +12,7 @@ namespace idx {
 constexpr int kHeads = 64;   // indexer heads the MFMA tiling is built for
 constexpr int kHeadDim = 128; // one 16x16x128 MFMA covers a whole head
 constexpr int kTile = 16;    // tokens per MFMA column tile
+constexpr int kInlineSplitMaxSegs = 1024; // decode without a schedule buffer: B at most this
 constexpr int kMaxSegs = 16000;      // schedule segments the builder scans in LDS (64000 B)
 constexpr int kTopkMaxW = 65536;     // in-register top-k row capacity
 constexpr int kPrefillRowsPerSeg = 7;  // query rows sharing one K stream in prefill

@@ -165,6 +165,73 @@ __device__ inline bool advance(const LogitsArgs &a, Walk &w) {
   return next_segment(a, w);
 }
 
+// Inclusive prefix sum over the wave's lanes.
+__device__ inline int32_t wave_incl_scan(int32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// The range of work group c when no schedule buffer is given: the wave
+// computes what the schedule builder would write for entries c and c + 1
+// (same costs: ceil(len / BK) blocks per non-empty sequence plus the decode
+// entry cost; range c starts at unit floor(c * N / n_ctas) of the N units),
+// from all B <= kInlineSplitMaxSegs lengths at once, 64 sequences per lane
+// slot.
+__device__ inline void own_range(const LogitsArgs &a, int c, Walk &w) {
+  constexpr int kChunks = kInlineSplitMaxSegs / 64;
+  const int lane = threadIdx.x & 63;
+  int32_t len[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) // every load first: one round trip
+    if (i * 64 < a.nseg) len[i] = 64 * i + lane < a.nseg ? a.lens[64 * i + lane] : 0;
+  int32_t pre[kChunks]; // exclusive prefix cost of sequence 64 i + lane
+  int32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (i * 64 < a.nseg) {
+      const int32_t L = len[i] > 0 ? len[i] : 0;
+      const int32_t nb = (L + a.block_tokens - 1) / a.block_tokens;
+      const int32_t cost = nb > 0 ? nb + kDecodeEntryCost : 0;
+      const int32_t incl = wave_incl_scan(cost);
+      pre[i] = total + incl - cost;
+      total += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  const int64_t N = total;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t T = ((int64_t)(c + e) * N) / a.n_ctas;
+    int32_t seg = a.nseg, blk = 0;
+    if (T < N) {
+      // the last sequence whose prefix is <= T holds unit T
+      int32_t cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i)
+        if (i * 64 < a.nseg)
+          cnt += __popcll(__ballot(64 * i + lane < a.nseg && pre[i] <= T));
+      seg = cnt - 1;
+      int32_t p = 0;
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i)
+        if (i == (seg >> 6)) p = __builtin_amdgcn_readlane(pre[i], seg & 63);
+      const int64_t u = T - p - kDecodeEntryCost;
+      blk = u > 0 ? (int32_t)u : 0;
+    }
+    if (e == 0) {
+      w.s = seg;
+      w.blk = blk;
+    } else {
+      w.se = seg;
+      w.be = blk;
+    }
+  }
+}
+
 // K operands of one block: TPB tiles of 16 tokens of one page.
 template <int TPB> struct KBlock {
   v8i kb[TPB];
@@ -362,12 +429,16 @@ template <int DT, int NROW, int TPB>
 __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   const int c = blockIdx.x;
   Walk w;
-  w.s = uniform_load(a.cta_info + 2 * c);
-  w.blk = uniform_load(a.cta_info + 2 * c + 1);
-  w.s = w.s > 0 ? w.s : 0; // a buffer never written by the builder must not index backwards
-  w.blk = w.blk > 0 ? w.blk : 0;
-  w.se = uniform_load(a.cta_info + 2 * c + 2);
-  w.be = uniform_load(a.cta_info + 2 * c + 3);
+  if (a.cta_info != nullptr) {
+    w.s = uniform_load(a.cta_info + 2 * c);
+    w.blk = uniform_load(a.cta_info + 2 * c + 1);
+    w.s = w.s > 0 ? w.s : 0; // a buffer never written by the builder must not index backwards
+    w.blk = w.blk > 0 ? w.blk : 0;
+    w.se = uniform_load(a.cta_info + 2 * c + 2);
+    w.be = uniform_load(a.cta_info + 2 * c + 3);
+  } else {
+    own_range(a, c, w);
+  }
   if (!in_range(a, w)) return;
   w.nb = (segment_length(a, w.s) + a.block_tokens - 1) / a.block_tokens;
   if (w.blk >= w.nb && !next_segment(a, w)) return; // empty or stale entry

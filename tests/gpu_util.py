@@ -51,9 +51,11 @@ class DeviceCase:
                                     c.scale_row_stride)
 
 
-def run_decode(dc: DeviceCase, n_ctas=None, fill=float("nan"), k=None, stream=None):
+def run_decode(dc: DeviceCase, n_ctas=None, fill=float("nan"), k=None, stream=None,
+               inline_split=False):
     """Schedule + logits + top-k of a decode case; returns (logits, idx, count)
-    as CPU tensors."""
+    as CPU tensors. inline_split: no schedule buffer (each work group computes
+    its own range)."""
     case = dc.case
     k = k or case.k
     R = case.R
@@ -64,8 +66,11 @@ def run_decode(dc: DeviceCase, n_ctas=None, fill=float("nan"), k=None, stream=No
     logits = torch.full((R, case.W), fill, dtype=torch.float32, device=dev)
     out = torch.empty((R, k), dtype=torch.int32, device=dev)
     cnt = torch.empty(R, dtype=torch.int32, device=dev)
-    idx.idx_build_schedule(dc.t["lens"], case.B, case.next_n, case.cache.page_size, n_ctas, cta,
-                           stream=stream)
+    if inline_split:
+        cta = None
+    else:
+        idx.idx_build_schedule(dc.t["lens"], case.B, case.next_n, case.cache.page_size, n_ctas,
+                               cta, stream=stream)
     idx.idx_paged_mqa_logits(dc.query, dc.kv, dc.t["block_tables"], case.block_tables.shape[1],
                              dc.t["lens"], case.B, case.next_n, cta, n_ctas, logits, case.W,
                              stream=stream)

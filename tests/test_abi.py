@@ -114,7 +114,8 @@ def test_logits_rejects_bad_cache(lib, mutate, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(n=0), idx.IDX_ERR_INVALID), (dict(n=5), idx.IDX_ERR_INVALID),
     (dict(B=0), idx.IDX_ERR_INVALID), (dict(B=16001), idx.IDX_ERR_INVALID),
-    (dict(cta=0), idx.IDX_ERR_INVALID), (dict(nc=0), idx.IDX_ERR_INVALID),
+    (dict(cta=0, B=1025), idx.IDX_ERR_INVALID),  # no schedule buffer: B <= 1024 only
+    (dict(nc=0), idx.IDX_ERR_INVALID),
     (dict(W=0), idx.IDX_ERR_INVALID), (dict(bts=0), idx.IDX_ERR_INVALID),
 ])
 def test_logits_rejects_bad_shapes(lib, kw, status):

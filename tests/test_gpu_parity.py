@@ -77,6 +77,28 @@ def test_schedule_split_does_not_change_results(n_ctas):
     assert torch.equal(o, ref_o)
 
 
+@pytest.mark.parametrize("B,next_n,P,n_ctas", [(9, 1, 64, 512), (9, 2, 32, 3), (64, 1, 64, 2048),
+                                               (130, 3, 256, 700), (1024, 1, 64, 1),
+                                               (1024, 2, 32, 5000)])
+def test_in_kernel_split_equals_the_schedule_buffer(B, next_n, P, n_ctas):
+    """Without a schedule buffer each work group computes its own range; the
+    logits and selections are bit-identical to the builder's split."""
+    log("inline split B %d next_n %d P %d n_ctas %d" % (B, next_n, P, n_ctas))
+    rng = np.random.default_rng(B + P)
+    hi = 3000 if B <= 130 else 600
+    lens = rng.integers(0, hi, size=B)
+    lens[rng.integers(0, B, size=max(1, B // 8))] = 0
+    lens[0] = hi - 1
+    case = synth.decode_case(lens.tolist(), next_n=next_n, P=P, k=64, W=3000, seed=410 + B)
+    dc = DeviceCase(case)
+    ref_l, ref_o, ref_c = run_decode(dc, n_ctas=n_ctas)
+    l, o, c = run_decode(dc, n_ctas=n_ctas, inline_split=True)
+    assert torch.equal(torch.nan_to_num(l, nan=7.0), torch.nan_to_num(ref_l, nan=7.0))
+    assert torch.equal(o, ref_o) and torch.equal(c, ref_c)
+    if B <= 64:
+        _check_decode(case, l, o, c, "inline split")
+
+
 def test_physical_page_permutation_gives_identical_bits():
     case = synth.decode_case(LENS, next_n=1, P=32, k=64, W=2304, seed=500)
     la, oa, _ = run_decode(DeviceCase(case))
