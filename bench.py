@@ -311,6 +311,99 @@ def prefill_bench(args, torch, idx, synth):
             "tflops_whole_call": flops / (ms * 1e-3) / 1e12}
 
 
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "prefill_logits_fp8_chunked_mfma_counters")
+FP8_MFMA_FLOPS = 16 * 16 * 128 * 2  # one v_mfma_f32_16x16x128_f8f6f4
+
+
+def prefill_source_digest():
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "device_common.h", "internal.h"):
+        with open(os.path.join(ROOT, "sparse_attention_indexer_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_mfma(pmc_dir):
+    """MFMA use of the prefill scoring kernel from one rocprofv3 run with
+    --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
+    of `--prefill-counters`: FP8 flops per dispatch = MFMA instructions x
+    16*16*128*2, over that dispatch's traced duration."""
+    import csv
+    import glob
+
+    def one(pattern):
+        files = glob.glob(os.path.join(pmc_dir, "**", pattern), recursive=True)
+        if not files:
+            raise SystemExit("no %s under %s" % (pattern, pmc_dir))
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    cnt = {}
+    for r in one("*counter_collection.csv"):
+        if "prefill_logits_kernel" not in r["Kernel_Name"]:
+            continue
+        d = cnt.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {}
+    for r in one("*kernel_trace.csv"):
+        if "prefill_logits_kernel" in r["Kernel_Name"]:
+            dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    rows = []
+    for did in sorted(cnt):
+        if did not in dur:
+            continue
+        c = cnt[did]
+        flops = c.get("SQ_INSTS_MFMA", 0.0) * FP8_MFMA_FLOPS
+        rows.append({"dispatch": did, "mfma_insts": c.get("SQ_INSTS_MFMA", 0.0),
+                     "mfma_busy_cycles": c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0),
+                     "grbm_gui_active": c.get("GRBM_GUI_ACTIVE", 0.0),
+                     "us": dur[did] * 1e6, "tflops": flops / dur[did] / 1e12})
+    big = [r for r in rows if r["mfma_insts"] >= 0.5 * max(x["mfma_insts"] for x in rows)]
+    avg = lambda key: sum(r[key] for r in big) / len(big)
+    summary = {
+        "kernel": "prefill_logits_kernel<FP8, 4 tiles> (first chunk: 15625 rows)",
+        "workload": "chunked prefill: 16384 rows over 4096 keys, causal (r+1)//4, page 64",
+        "kernel_source_digest": prefill_source_digest(),
+        "commands": [
+            "rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+            "--kernel-trace --output-format csv -d <dir> -o run -- "
+            "python3 -u bench.py --prefill-counters",
+            "python3 bench.py --summarize-mfma <dir>",
+        ],
+        "dispatches": big,
+        "mfma_insts_per_dispatch": avg("mfma_insts"),
+        "us_per_dispatch": avg("us"),
+        "fp8_tflops": avg("tflops"),
+        "fp8_mfma_frac": avg("tflops") / FP8_MFMA_PEAK_TFLOPS,
+    }
+    with open(MFMA_SUMMARY + ".json", "w") as fh:
+        json.dump(summary, fh, indent=1)
+    with open(MFMA_SUMMARY + ".md", "w") as fh:
+        fh.write("# MFMA use of the chunked-prefill scoring kernel (rocprofv3 PMC)\n\n")
+        fh.write("Commands (repository root, one MI355X):\n\n```\n%s\n```\n\n" %
+                 "\n".join(summary["commands"]))
+        fh.write("`bench.py --prefill-counters` runs the 16384-row prefill call three times "
+                 "(budget 256e6 B: a 15625-row chunk and a 759-row chunk). Rows below are the "
+                 "first-chunk dispatches.\n\n")
+        fh.write("| dispatch | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | "
+                 "traced us | FP8 TFLOP/s |\n|---|---|---|---|---|---|\n")
+        for r in big:
+            fh.write("| %d | %s | %s | %s | %.1f | %.0f |\n" % (
+                r["dispatch"], f"{r['mfma_insts']:,.0f}", f"{r['mfma_busy_cycles']:,.0f}",
+                f"{r['grbm_gui_active']:,.0f}", r["us"], r["tflops"]))
+        fh.write("\nFP8 flops = SQ_INSTS_MFMA x %d (one 16x16x128 FP8 MFMA); average %.0f "
+                 "TFLOP/s = %.1f%% of the 5.0 PFLOP/s dense FP8 peak. Kernel source digest: "
+                 "`%s`.\n" % (FP8_MFMA_FLOPS, summary["fp8_tflops"], 100 * summary["fp8_mfma_frac"],
+                               summary["kernel_source_digest"]))
+    print(json.dumps({k: v for k, v in summary.items() if k != "dispatches"}, indent=1))
+
+
+def prefill_counter_run(args, torch, idx, synth):
+    """For rocprofv3 --pmc: three eager chunked-prefill calls."""
+    args.steps = 12
+    prefill_bench(args, torch, idx, synth)
+
+
 def kv_write_bench(args, torch, idx, synth):
     """K-cache writer: 65536 new bf16 key rows quantized to FP8 and scattered
     over a 1024-page pool of 64-row pages (rows in a random slot order)."""
@@ -432,6 +525,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--prefill-counters", action="store_true",
+                    help="eager prefill calls only (for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="write the profiles/ MFMA summary from a --prefill-counters PMC run")
     ap.add_argument("--counters", action="store_true",
                     help="only a reference copy + scoring launches, for rocprofv3 --pmc runs")
     ap.add_argument("--all-workloads", action="store_true",
@@ -441,6 +538,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -461,6 +561,9 @@ def main():
 
     if args.counters:
         counter_run(args, torch, idx, synth)
+        return
+    if args.prefill_counters:
+        prefill_counter_run(args, torch, idx, synth)
         return
     d = decode_bench(args, torch, idx, synth)
     log("decode (%s split): step %.3f ms, scoring kernel %.3f ms avg (%.3f min), %.0f GB/s" % (
@@ -544,6 +647,16 @@ def main():
             "fp8_tflops_whole_call": pre["tflops_whole_call"],
             "fp8_mfma_frac_whole_call": pre["tflops_whole_call"] / FP8_MFMA_PEAK_TFLOPS,
         }
+        try:
+            with open(MFMA_SUMMARY + ".json") as fh:
+                mf = json.load(fh)
+            if mf.get("kernel_source_digest") == prefill_source_digest():
+                line["prefill"]["scoring_kernel_counters"] = {
+                    "fp8_tflops": mf["fp8_tflops"], "fp8_mfma_frac": mf["fp8_mfma_frac"],
+                    "us_per_dispatch": mf["us_per_dispatch"],
+                    "source": "profiles/prefill_logits_fp8_chunked_mfma_counters.md"}
+        except (OSError, ValueError, KeyError):
+            pass
     if alt:
         line["decode_with_schedule_buffer"] = {
             "ms_per_step": alt["step_ms"], "scoring_kernel_us": alt["kern_avg_ms"] * 1e3,

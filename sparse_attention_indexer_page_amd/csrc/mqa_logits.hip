@@ -155,7 +155,7 @@ __device__ inline bool next_segment(const LogitsArgs &a, Walk &w) {
   while (true) {
     ++w.s;
     if (!in_range(a, w)) return false;
-    w.nb = (segment_length(a, w.s) + a.block_tokens - 1) / a.block_tokens;
+    w.nb = (segment_length(a, w.s) + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
     if (w.nb > 0) return true;
   }
 }
@@ -165,14 +165,18 @@ __device__ inline bool advance(const LogitsArgs &a, Walk &w) {
   return next_segment(a, w);
 }
 
-// Inclusive prefix sum over the wave's lanes.
+// Inclusive prefix sum over the wave's lanes with DPP moves (no LDS round
+// trips): shifts by 1, 2, 4, 8 within each 16-lane row (lanes shifted in from
+// outside the row add 0), then row 0's total into rows 1 and 3 and row 1's
+// into rows 2 and 3 (row_bcast 15), then the first half's into the second
+// (row_bcast 31).
 __device__ inline int32_t wave_incl_scan(int32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false); // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false); // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false); // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false); // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
   return v;
 }
 
@@ -182,7 +186,7 @@ __device__ inline int32_t wave_incl_scan(int32_t v) {
 // entry cost; range c starts at unit floor(c * N / n_ctas) of the N units),
 // from all B <= kInlineSplitMaxSegs lengths at once, 64 sequences per lane
 // slot.
-__device__ inline void own_range(const LogitsArgs &a, int c, Walk &w) {
+__device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   constexpr int kChunks = kInlineSplitMaxSegs / 64;
   const int lane = threadIdx.x & 63;
   int32_t len[kChunks];
@@ -195,7 +199,7 @@ __device__ inline void own_range(const LogitsArgs &a, int c, Walk &w) {
   for (int i = 0; i < kChunks; ++i) {
     if (i * 64 < a.nseg) {
       const int32_t L = len[i] > 0 ? len[i] : 0;
-      const int32_t nb = (L + a.block_tokens - 1) / a.block_tokens;
+      const int32_t nb = (L + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens); // 32 or 64
       const int32_t cost = nb > 0 ? nb + kDecodeEntryCost : 0;
       const int32_t incl = wave_incl_scan(cost);
       pre[i] = total + incl - cost;
@@ -203,6 +207,7 @@ __device__ inline void own_range(const LogitsArgs &a, int c, Walk &w) {
     }
   }
   const int64_t N = total;
+  int32_t len0 = 0; // length of the range's first sequence
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int64_t T = ((int64_t)(c + e) * N) / a.n_ctas;
@@ -218,7 +223,10 @@ __device__ inline void own_range(const LogitsArgs &a, int c, Walk &w) {
       int32_t p = 0;
 #pragma unroll
       for (int i = 0; i < kChunks; ++i)
-        if (i == (seg >> 6)) p = __builtin_amdgcn_readlane(pre[i], seg & 63);
+        if (i == (seg >> 6)) {
+          p = __builtin_amdgcn_readlane(pre[i], seg & 63);
+          if (e == 0) len0 = __builtin_amdgcn_readlane(len[i], seg & 63);
+        }
       const int64_t u = T - p - kDecodeEntryCost;
       blk = u > 0 ? (int32_t)u : 0;
     }
@@ -230,6 +238,7 @@ __device__ inline void own_range(const LogitsArgs &a, int c, Walk &w) {
       w.be = blk;
     }
   }
+  return len0 > 0 ? len0 : 0;
 }
 
 // K operands of one block: TPB tiles of 16 tokens of one page.
@@ -255,16 +264,17 @@ __device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp) {
 // the block loop then has the same number of loads in flight, which keeps the
 // compiler's wait counts partial (a path without them would force it to wait
 // for every load, including the next block's, before the first MFMA).
+// The block's page comes from the caller (pg < 0: nothing to load).
 template <int DT, int TPB>
-__device__ inline void issue_block(const LogitsArgs &a, const Walk &w, bool live, KBlock<TPB> &kb) {
+__device__ inline void issue_block_page(const LogitsArgs &a, int blk, int64_t pg,
+                                        KBlock<TPB> &kb) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int col = lane & 15;
   const int P = a.page_size;
-  const int t0 = w.blk * a.block_tokens;
+  const int t0 = blk * a.block_tokens;
   const int lp = t0 / P;
   const int slot0 = t0 - lp * P;
-  int64_t pg = live ? page_of(a, w.s, lp) : -1;
   const bool valid = pg >= 0 && pg < a.num_pages;
   if (!valid) pg = 0;
   const uint32_t page_bytes = (uint32_t)(P * a.row_stride);
@@ -291,6 +301,12 @@ __device__ inline void issue_block(const LogitsArgs &a, const Walk &w, bool live
       kb.ks[ti] = load4(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
     }
   }
+}
+
+template <int DT, int TPB>
+__device__ inline void issue_block(const LogitsArgs &a, const Walk &w, bool live, KBlock<TPB> &kb) {
+  const int lp = (w.blk * a.block_tokens) / a.page_size;
+  issue_block_page<DT, TPB>(a, w.blk, live ? page_of(a, w.s, lp) : -1, kb);
 }
 
 // MFMAs of one 16-token tile against every head tile of every row.
@@ -429,6 +445,7 @@ template <int DT, int NROW, int TPB>
 __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   const int c = blockIdx.x;
   Walk w;
+  int32_t len0;
   if (a.cta_info != nullptr) {
     w.s = uniform_load(a.cta_info + 2 * c);
     w.blk = uniform_load(a.cta_info + 2 * c + 1);
@@ -436,17 +453,25 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
     w.blk = w.blk > 0 ? w.blk : 0;
     w.se = uniform_load(a.cta_info + 2 * c + 2);
     w.be = uniform_load(a.cta_info + 2 * c + 3);
+    if (!in_range(a, w)) return;
+    len0 = segment_length(a, w.s);
   } else {
-    own_range(a, c, w);
+    len0 = own_range(a, c, w);
+    if (!in_range(a, w)) return;
   }
-  if (!in_range(a, w)) return;
-  w.nb = (segment_length(a, w.s) + a.block_tokens - 1) / a.block_tokens;
-  if (w.blk >= w.nb && !next_segment(a, w)) return; // empty or stale entry
-
-  // the first block's K loads go out before the query's, so the two
-  // latencies overlap
+  // The first block's page is read together with the segment's length (the
+  // table entry exists whether or not the block does), so the first K loads
+  // wait for one round trip less; they go out before the query's, so those
+  // two latencies overlap as well.
+  const int64_t pg0 = page_of(a, w.s, (w.blk * a.block_tokens) / a.page_size);
+  w.nb = (len0 + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
   KBlock<TPB> A, B;
-  issue_block<DT, TPB>(a, w, true, A);
+  if (w.blk < w.nb) {
+    issue_block_page<DT, TPB>(a, w.blk, pg0, A);
+  } else { // empty or stale entry
+    if (!next_segment(a, w)) return;
+    issue_block<DT, TPB>(a, w, true, A);
+  }
   QRegs<DT, NROW> Q;
   int32_t L = enter_segment<DT, NROW>(a, w.s, Q);
   __shared__ OutStage<NROW> st;
