@@ -360,6 +360,10 @@ def summarize_mfma(pmc_dir):
                      "us": dur[did] * 1e6, "tflops": flops / dur[did] / 1e12})
     big = [r for r in rows if r["mfma_insts"] >= 0.5 * max(x["mfma_insts"] for x in rows)]
     avg = lambda key: sum(r[key] for r in big) / len(big)
+    # MFMA busy cycles are summed over the 1024 SIMDs (one 16x16x128 FP8 MFMA
+    # keeps a SIMD busy 32 cycles); against the traced duration at the
+    # 2.4 GHz peak engine clock this is a lower bound on the busy fraction.
+    busy_frac = avg("mfma_busy_cycles") / (1024 * avg("us") * 1e-6 * 2.4e9)
     summary = {
         "kernel": "prefill_logits_kernel<FP8, 4 tiles> (first chunk: 15625 rows)",
         "workload": "chunked prefill: 16384 rows over 4096 keys, causal (r+1)//4, page 64",
@@ -375,6 +379,7 @@ def summarize_mfma(pmc_dir):
         "us_per_dispatch": avg("us"),
         "fp8_tflops": avg("tflops"),
         "fp8_mfma_frac": avg("tflops") / FP8_MFMA_PEAK_TFLOPS,
+        "mfma_busy_frac_at_2p4ghz": busy_frac,
     }
     with open(MFMA_SUMMARY + ".json", "w") as fh:
         json.dump(summary, fh, indent=1)
@@ -392,9 +397,12 @@ def summarize_mfma(pmc_dir):
                 r["dispatch"], f"{r['mfma_insts']:,.0f}", f"{r['mfma_busy_cycles']:,.0f}",
                 f"{r['grbm_gui_active']:,.0f}", r["us"], r["tflops"]))
         fh.write("\nFP8 flops = SQ_INSTS_MFMA x %d (one 16x16x128 FP8 MFMA); average %.0f "
-                 "TFLOP/s = %.1f%% of the 5.0 PFLOP/s dense FP8 peak. Kernel source digest: "
-                 "`%s`.\n" % (FP8_MFMA_FLOPS, summary["fp8_tflops"], 100 * summary["fp8_mfma_frac"],
-                               summary["kernel_source_digest"]))
+                 "TFLOP/s = %.1f%% of the 5.0 PFLOP/s dense FP8 peak. SQ_VALU_MFMA_BUSY_CYCLES "
+                 "over 1024 SIMDs x traced duration x 2.4 GHz: %.1f%% busy (a lower bound if the "
+                 "engine clock ran below 2.4 GHz). GRBM_GUI_ACTIVE is listed as read. Kernel "
+                 "source digest: `%s`.\n" % (
+                     FP8_MFMA_FLOPS, summary["fp8_tflops"], 100 * summary["fp8_mfma_frac"],
+                     100 * busy_frac, summary["kernel_source_digest"]))
     print(json.dumps({k: v for k, v in summary.items() if k != "dispatches"}, indent=1))
 
 

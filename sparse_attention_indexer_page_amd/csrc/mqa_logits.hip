@@ -210,7 +210,11 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   int32_t len0 = 0; // length of the range's first sequence
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int64_t T = ((int64_t)(c + e) * N) / a.n_ctas;
+    // floor((c + e) N / n_ctas) through one double division: the numerator
+    // (< 2^51) and n_ctas (<= 2^20) are exact, and a non-integer quotient
+    // (< 2^31) lies at least 1/n_ctas from an integer, far beyond the
+    // division's rounding error (< 2^-22), so truncation gives the floor
+    const int64_t T = (int64_t)((double)((int64_t)(c + e) * N) / (double)a.n_ctas);
     int32_t seg = a.nseg, blk = 0;
     if (T < N) {
       // the last sequence whose prefix is <= T holds unit T
