@@ -24,10 +24,12 @@ def _built():
     ensure_built()
 
 
-def _step(dc, off_dev, max_q, n_ctas, logits, ve, out, cnt):
+def _step(dc, off_dev, max_q, n_ctas, logits, ve, out, cnt, inline_split=False):
     case = dc.case
-    cta = torch.empty(idx.idx_schedule_ints(n_ctas), dtype=torch.int32, device="cuda")
-    idx.idx_build_schedule(dc.t["lens"], case.B, max_q, case.cache.page_size, n_ctas, cta)
+    cta = None
+    if not inline_split:
+        cta = torch.empty(idx.idx_schedule_ints(n_ctas), dtype=torch.int32, device="cuda")
+        idx.idx_build_schedule(dc.t["lens"], case.B, max_q, case.cache.page_size, n_ctas, cta)
     idx.idx_paged_mqa_logits_varlen(dc.query, dc.kv, dc.t["block_tables"],
                                     case.block_tables.shape[1], dc.t["lens"], off_dev, case.B,
                                     max_q, cta, n_ctas, logits, case.W)
@@ -66,10 +68,11 @@ def _check(case, off, max_q, logits, ve, out, cnt):
         check_topk_band(o[r], ref[r], e, case.k, "row %d" % r)
 
 
-@pytest.mark.parametrize("dtype,P,max_q", [(synth.FP8, 64, 4), (synth.FP8, 32, 3),
-                                           (synth.MXFP4, 256, 2), (synth.FP8, 256, 1)])
-def test_varlen_matches_oracle(dtype, P, max_q):
-    log("varlen dtype %d P %d max_q %d" % (dtype, P, max_q))
+@pytest.mark.parametrize("dtype,P,max_q,inline_split", [
+    (synth.FP8, 64, 4, False), (synth.FP8, 32, 3, True), (synth.MXFP4, 256, 2, False),
+    (synth.MXFP4, 64, 3, True), (synth.FP8, 256, 1, False)])
+def test_varlen_matches_oracle(dtype, P, max_q, inline_split):
+    log("varlen dtype %d P %d max_q %d inline %d" % (dtype, P, max_q, inline_split))
     rng = np.random.default_rng(300 + P + max_q)
     B = 24
     lens = rng.integers(0, 2500, size=B).astype(np.int32)
@@ -80,7 +83,7 @@ def test_varlen_matches_oracle(dtype, P, max_q):
     off = synth.ragged_offsets(rng, B, max_q)
     dc = DeviceCase(case)
     bufs = _buffers(case, max_q)
-    _step(dc, torch.from_numpy(off).cuda(), max_q, 300, *bufs)
+    _step(dc, torch.from_numpy(off).cuda(), max_q, 300, *bufs, inline_split=inline_split)
     torch.cuda.synchronize()
     _check(case, off, max_q, *bufs)
 
