@@ -70,11 +70,18 @@ typedef enum idx_dtype {
  *          q_scale E8M0  [R][H][D/32] (required)
  *   weights fp32 [R][H] (per-row, per-head indexer weights; any sign).
  * q must be 16-byte aligned. */
+/* Query flag: idx_paged_mqa_logits / idx_paged_mqa_logits_varlen also write
+ * -inf to every column [E_r, W) of every row of the logits buffer (E_r = 0
+ * for a ragged buffer row no sequence owns), so the whole buffer is defined
+ * for a consumer that reads full rows; one more pass over the buffer. The
+ * prefill entry and idx_quantize_query ignore it. */
+#define IDX_QUERY_FILL_NEG_INF 1
+
 typedef struct idx_query {
     int32_t dtype;     /* idx_dtype */
     int32_t num_heads; /* H; must be 64 */
     int32_t head_dim;  /* D; must be 128 */
-    int32_t reserved;  /* set to 0 */
+    int32_t flags;     /* 0 or IDX_QUERY_FILL_NEG_INF; other bits are rejected */
     const void *q;
     const void *q_scale;
     const float *weights;
@@ -134,7 +141,8 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
 /*
  * Decode scores ("mqa-logits"). Query row r = b*next_n + j (j < next_n) of
  * sequence b sees E_r = max(0, context_lens[b] - (next_n - 1 - j)) tokens;
- * for t < E_r it writes logits[r*W + t]. Columns t >= E_r are not written.
+ * for t < E_r it writes logits[r*W + t]. Columns t >= E_r are not written
+ * (unless q->flags has IDX_QUERY_FILL_NEG_INF: then they are set to -inf).
  *
  *   q, kv          descriptors above (host pointers to structs holding
  *                  device pointers); kv->dtype == q->dtype

@@ -7,7 +7,8 @@ first call does, and fails loudly if it has not been built.
 """
 from .binding import (  # noqa: F401
     EXPORTS, IDX_ERR_HIP, IDX_ERR_INVALID, IDX_ERR_UNSUPPORTED, IDX_ERR_WORKSPACE,
-    IDX_FP8_E4M3, IDX_KIN_BF16, IDX_KIN_F32, IDX_MXFP4, IDX_OK, IdxError, KVCache, Query,
+    IDX_FP8_E4M3, IDX_KIN_BF16, IDX_KIN_F32, IDX_MXFP4, IDX_OK, IDX_QUERY_FILL_NEG_INF, IdxError,
+    KVCache, Query,
     idx_build_schedule, idx_kv_cache_write,
     idx_last_error_message, idx_paged_mqa_logits, idx_paged_mqa_logits_varlen,
     idx_prefill_chunked_topk,

@@ -23,6 +23,7 @@ IDX_ERR_HIP = 4
 IDX_FP8_E4M3 = 1
 IDX_MXFP4 = 2
 
+IDX_QUERY_FILL_NEG_INF = 1
 IDX_KIN_F32 = 0
 IDX_KIN_BF16 = 1
 
@@ -46,7 +47,7 @@ class IdxError(RuntimeError):
 class Query(ctypes.Structure):
     """struct idx_query."""
     _fields_ = [("dtype", ctypes.c_int32), ("num_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
                 ("weights", ctypes.c_void_p)]
 
@@ -141,8 +142,8 @@ def stream_handle(stream) -> int | None:
     return stream.cuda_stream
 
 
-def make_query(dtype, q, q_scale, weights, num_heads=64, head_dim=128) -> Query:
-    return Query(dtype, num_heads, head_dim, 0, ptr(q), ptr(q_scale), ptr(weights))
+def make_query(dtype, q, q_scale, weights, num_heads=64, head_dim=128, flags=0) -> Query:
+    return Query(dtype, num_heads, head_dim, flags, ptr(q), ptr(q_scale), ptr(weights))
 
 
 def make_kv_cache(dtype, page_size, num_pages, data, page_stride_bytes, row_stride_bytes,

@@ -43,6 +43,8 @@ idx_status check_query(const idx_query *q) {
     return fail(IDX_ERR_UNSUPPORTED, "num_heads %d unsupported (64 only)", q->num_heads);
   if (q->head_dim != idx::kHeadDim)
     return fail(IDX_ERR_UNSUPPORTED, "head_dim %d unsupported (128 only)", q->head_dim);
+  if (q->flags & ~IDX_QUERY_FILL_NEG_INF)
+    return fail(IDX_ERR_INVALID, "query flags 0x%x has unknown bits", (unsigned)q->flags);
   if (!q->q || !q->weights) return fail(IDX_ERR_INVALID, "q or weights pointer is null");
   if (!aligned(q->q, 16)) return fail(IDX_ERR_INVALID, "q must be 16-byte aligned");
   if (!aligned(q->weights, 16)) return fail(IDX_ERR_INVALID, "weights must be 16-byte aligned");
@@ -219,6 +221,10 @@ idx_status decode_logits(const idx_query *q, const idx_kv_cache *kv, const int32
   hipError_t e = q->dtype == IDX_FP8_E4M3 ? idx::launch_logits_fp8_decode(a, s)
                                           : idx::launch_logits_mxfp4_decode(a, s);
   if (e != hipSuccess) return hip_fail(e, "logits launch");
+  if (q->flags & IDX_QUERY_FILL_NEG_INF) {
+    e = idx::launch_fill_tail(context_lens, row_offsets, B, next_n, W, logits, s);
+    if (e != hipSuccess) return hip_fail(e, "logits tail launch");
+  }
   return ok();
 }
 

@@ -120,6 +120,8 @@ struct QQuantArgs {
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t s);
+hipError_t launch_fill_tail(const int32_t *lens, const int32_t *row_offsets, int32_t B, int32_t n,
+                            int64_t W, float *logits, hipStream_t s);
 hipError_t launch_varlen_windows(const int32_t *lens, const int32_t *row_offsets, int32_t B,
                                  int32_t max_q, int32_t *visible_end, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);

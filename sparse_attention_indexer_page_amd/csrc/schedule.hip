@@ -126,33 +126,61 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
 // len_b - (n_b - 1 - j) keys. Every row of the [B * max_q] buffer is written:
 // rows no sequence owns get 0, so a fixed-shape top-k over the whole buffer
 // selects nothing for them.
+// Visible length of row r: with offsets, the ragged rule above (0 for a row
+// no sequence owns); without, row r = b*n + j of the rectangular step.
+__device__ inline int32_t row_window(const int32_t *lens, const int32_t *off, int32_t B,
+                                     int32_t n_max, int64_t r) {
+  if (off == nullptr) {
+    const int64_t b = r / n_max;
+    const int32_t j = (int32_t)(r - b * n_max);
+    const int32_t e = lens[b] - (n_max - 1 - j);
+    return e > 0 ? e : 0;
+  }
+  // last sequence b with off[b] <= r (offsets are non-decreasing)
+  if (off[0] > r) return 0;
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  const int32_t base = off[lo];
+  int32_t n = off[lo + 1] - base;
+  n = n < 0 ? 0 : (n > n_max ? n_max : n);
+  const int32_t j = (int32_t)(r - base);
+  if (j >= n) return 0;
+  const int32_t len = lens[lo] > 0 ? lens[lo] : 0;
+  const int32_t e = len - (n - 1 - j);
+  return e > 0 ? e : 0;
+}
+
 __global__ __launch_bounds__(256) void varlen_windows_kernel(const int32_t *lens,
                                                              const int32_t *off, int32_t B,
                                                              int32_t max_q, int32_t *ve) {
   const int64_t rows = (int64_t)B * max_q;
-  for (int64_t r = blockIdx.x * 256ll + threadIdx.x; r < rows; r += (int64_t)gridDim.x * 256) {
-    // last sequence b with off[b] <= r (offsets are non-decreasing)
-    int lo = 0, hi = B;
-    if (off[0] > r) {
-      ve[r] = 0;
-      continue;
-    }
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= r) lo = mid;
-      else hi = mid;
-    }
-    const int32_t base = off[lo];
-    int32_t n = off[lo + 1] - base;
-    n = n < 0 ? 0 : (n > max_q ? max_q : n);
-    const int32_t j = (int32_t)(r - base);
-    int32_t e = 0;
-    if (j < n) {
-      const int32_t len = lens[lo] > 0 ? lens[lo] : 0;
-      e = len - (n - 1 - j);
-      e = e > 0 ? e : 0;
-    }
-    ve[r] = e;
+  for (int64_t r = blockIdx.x * 256ll + threadIdx.x; r < rows; r += (int64_t)gridDim.x * 256)
+    ve[r] = row_window(lens, off, B, max_q, r);
+}
+
+// -inf into columns [E_r, W) of every row of a [B * n][W] logits buffer (the
+// opt-in that makes the whole buffer defined). Work group (x, y): row y,
+// columns [1024 x, 1024 x + 1024), four per thread.
+__global__ __launch_bounds__(256) void fill_tail_kernel(const int32_t *lens, const int32_t *off,
+                                                        int32_t B, int32_t n, int64_t W,
+                                                        float *logits) {
+  const int64_t r = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * 1024 + 4 * threadIdx.x;
+  if (t0 >= W) return;
+  int64_t e = row_window(lens, off, B, n, r);
+  e = e < W ? e : W;
+  float *row = logits + r * W;
+  const float ninf = -__builtin_huge_valf();
+  if ((W & 3) == 0 && t0 >= e && t0 + 4 <= W) {
+    *reinterpret_cast<float4 *>(row + t0) = float4{ninf, ninf, ninf, ninf};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t0 + i >= e && t0 + i < W) row[t0 + i] = ninf;
   }
 }
 
@@ -164,6 +192,14 @@ hipError_t launch_varlen_windows(const int32_t *lens, const int32_t *row_offsets
   const int64_t g = (rows + 255) / 256;
   hipLaunchKernelGGL(varlen_windows_kernel, dim3(g < 1024 ? (unsigned)g : 1024u), dim3(256), 0,
                      s, lens, row_offsets, B, max_q, visible_end);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_tail(const int32_t *lens, const int32_t *row_offsets, int32_t B, int32_t n,
+                            int64_t W, float *logits, hipStream_t s) {
+  const int64_t gx = (W + 1023) / 1024;
+  hipLaunchKernelGGL(fill_tail_kernel, dim3((unsigned)gx, (unsigned)(B * n)), dim3(256), 0, s,
+                     lens, row_offsets, B, n, W, logits);
   return hipGetLastError();
 }
 

@@ -275,3 +275,10 @@ def test_varlen_entry_points_reject_bad_arguments(lib):
     assert L.idx_varlen_windows(0x5000, 0x8000, 16001, 2, 0x9000, None) == idx.IDX_ERR_INVALID
     assert L.idx_varlen_windows(0x5002, 0x8000, 2, 2, 0x9000, None) == idx.IDX_ERR_INVALID
     assert idx.idx_last_error_message() != ""
+
+
+@pytest.mark.parametrize("flags", [2, 0x80000000 - (1 << 32), 3])
+def test_logits_rejects_unknown_query_flags(lib, flags):
+    q = binding.Query(1, 64, 128, flags, 0x1000, 0x2000, 0x3000)
+    assert _logits(q, _kv()) == idx.IDX_ERR_INVALID
+    assert "flags" in idx.idx_last_error_message()

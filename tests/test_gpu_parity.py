@@ -266,3 +266,23 @@ def test_prefill_global_indices_in_the_one_wave_top_k():
     _, og = run_prefill(dc, budget=4 * case.W * T, index_base=77)
     assert torch.equal(og, torch.where(out >= 0, out + 77, out))
     assert int((out >= 0).sum(dim=1).min()) == 1  # row 0 sees one token
+
+
+@pytest.mark.parametrize("next_n", [1, 3])
+def test_fill_flag_sets_the_tail_to_minus_inf(next_n):
+    """With IDX_QUERY_FILL_NEG_INF the columns [E_r, W) of every row read -inf
+    and the visible columns are bit-identical to a run without the flag."""
+    log("fill flag next_n %d" % next_n)
+    case = synth.decode_case([0, 1, 5, 300, 1999], next_n=next_n, P=32, k=16, W=2003, seed=960)
+    dc = DeviceCase(case)
+    ref_l, ref_o, _ = run_decode(dc, n_ctas=64)
+    dc.query = idx.make_query(case.dtype, dc.t["q"], dc.t["q_scale"], dc.t["w"],
+                              flags=idx.IDX_QUERY_FILL_NEG_INF)
+    l, o, _ = run_decode(dc, n_ctas=64, inline_split=True)
+    lg, rl = l.numpy(), ref_l.numpy()
+    for r in range(case.R):
+        b, j = divmod(r, next_n)
+        e = max(0, int(case.lens[b]) - (next_n - 1 - j))
+        assert np.array_equal(lg[r, :e], rl[r, :e])
+        assert np.all(np.isneginf(lg[r, e:])), "row %d tail" % r
+    assert torch.equal(o, ref_o)

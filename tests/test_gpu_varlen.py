@@ -145,3 +145,24 @@ def test_varlen_graph_replays_new_offsets():
         torch.cuda.synchronize()
         log("varlen graph step %d: %d rows" % (step, int(off[-1])))
         _check(case, off, max_q, logits, ve, out, cnt)
+
+
+def test_varlen_fill_flag_defines_every_row():
+    """With IDX_QUERY_FILL_NEG_INF every row of the B*max_q buffer is defined:
+    owned rows read -inf past their window, unowned rows are all -inf."""
+    log("varlen fill flag")
+    max_q = 3
+    case = synth.decode_case([40, 0, 700, 65, 3], next_n=max_q, P=64, k=32, W=1000, seed=330)
+    off = np.array([0, 2, 2, 5, 6, 7], dtype=np.int32)
+    dc = DeviceCase(case)
+    dc.query = idx.make_query(case.dtype, dc.t["q"], dc.t["q_scale"], dc.t["w"],
+                              flags=idx.IDX_QUERY_FILL_NEG_INF)
+    logits, ve, out, cnt = _buffers(case, max_q)
+    _step(dc, torch.from_numpy(off).cuda(), max_q, 50, logits, ve, out, cnt)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    E = oracle.varlen_windows(case.lens, off, case.B * max_q)
+    assert not np.isnan(lg).any(), "a logit was left unwritten"
+    for r in range(case.B * max_q):
+        assert np.all(np.isneginf(lg[r, E[r]:])), "row %d" % r
+        assert np.all(np.isfinite(lg[r, :E[r]]))
