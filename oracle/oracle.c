@@ -44,6 +44,14 @@
  *     E_r = max(0, len_b - (next_n-1-j)) (reading adopted: the last row of a
  *     sequence sees the whole context, each earlier row one token less);
  *   - prefill: E_r = visible_end[r], given per row.
+ *   - ragged decode: sequence b owns the packed rows [off[b], off[b+1]) and
+ *     its row j sees max(0, len_b - (n_b-1-j)), the rule above with next_n
+ *     replaced by the sequence's own row count (section at the end).
+ *
+ * Also here, each in its own section below with its readings: the K-cache
+ * writer's encoders (FP8 row scale amax/448, E4M3 nearest with ties to even;
+ * MXFP4 per-32 OCP MX exponent and E2M1 nearest with ties to even) and the
+ * query quantizer with the weight fold.
  */
 #include <math.h>
 #include <stdint.h>
