@@ -65,6 +65,27 @@ __device__ inline int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// Smallest key in (lo, hi] whose bin (a monotone non-decreasing function of
+// the key) is at least b, given that hi's is: a 64-way search, each lane
+// testing one evenly spaced key per round (at most six rounds for 32-bit
+// keys). lo itself is never evaluated. Wave-uniform result.
+template <typename BinOf>
+__device__ __forceinline__ uint32_t first_key_in_bin_at_least(uint32_t lo, uint32_t hi, uint32_t b,
+                                                             BinOf bin_of) {
+  const int lane = threadIdx.x & 63;
+  while (hi - lo > 1u) {
+    const uint32_t step = (hi - lo + 63u) / 64u;
+    const uint32_t off = (uint32_t)(lane + 1) * step; // <= hi - lo + 63: no wrap below 2^32
+    const uint32_t x = off >= hi - lo ? hi : lo + off;
+    const uint64_t m = __ballot(bin_of(x) >= b); // false ... false, true ... true (lane 63: hi)
+    const int f = (int)__builtin_ctzll(m);
+    const uint32_t nhi = __builtin_amdgcn_readlane(x, f);
+    lo = f == 0 ? lo : __builtin_amdgcn_readlane(x, f - 1);
+    hi = nhi;
+  }
+  return hi;
+}
+
 constexpr int kCandCap = 4096; // keys of the first pass's bin refined in LDS
 
 constexpr int kRankCap = 64; // candidates ranked directly by one wave
@@ -212,8 +233,9 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   const float hr = key_float(kmax) * 0.5f - h0;
   const float scale = (float)kBins / hr;
   if (hr > 0.f && scale < 3.0e38f) {
+    // one explicit FMA, so every evaluation of a key's bin rounds alike
     auto vbin = [&](uint32_t kk) -> uint32_t {
-      const float x = (key_float(kk) * 0.5f - h0) * scale;
+      const float x = __builtin_fmaf(key_float(kk), 0.5f, -h0) * scale;
       return (uint32_t)fminf(x, (float)(kBins - 1));
     };
     uint32_t bin;
@@ -228,44 +250,14 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
         bin, above, inbin);
     need -= above;
     cand = inbin;
-    uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
-    if (inbin == need || inbin > kCandCap) {
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        uint32_t kk = key[i];
-        asm volatile("" : "+v"(kk)); // recompute the bin rather than keep IPT of them live
-        if (kk != 0u && vbin(kk) == bin) {
-          bmin = kk < bmin ? kk : bmin;
-          bmax = kk > bmax ? kk : bmax;
-        }
-      }
-    } else {
-      // compact the bin's keys into LDS, then take their extremes there
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        uint32_t kk = key[i];
-        asm volatile("" : "+v"(kk));
-        const bool c = kk != 0u && vbin(kk) == bin;
-        const uint64_t m = __ballot(c);
-        if (m) {
-          uint32_t at = 0;
-          if (lane == 0) at = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
-          at = __shfl(at, 0, 64);
-          if (c) sm.cand[at + lanes_below(m)] = kk;
-        }
-      }
-      __syncthreads();
-      for (int c = tid; c < inbin; c += NT) {
-        const uint32_t x = sm.cand[c];
-        bmin = x < bmin ? x : bmin;
-        bmax = x > bmax ? x : bmax;
-      }
-      in_lds = true;
-      nc = inbin;
-    }
-    block_max_min<NT>(sm, bmax, bmin);
-    lo = bmin; // the bin's keys are exactly those in [lo, hi]
-    hi = bmax;
+    // The bin's keys form one key interval [lo, hi] (the bin is monotone in
+    // the key); every wave finds its ends from the uniform kmin, kmax and bin
+    // alike, so no pass over the keys and no barrier. The bin is not empty,
+    // so its first key is <= kmax and has bin exactly `bin`.
+    lo = first_key_in_bin_at_least(kmin - 1u, kmax, bin, vbin);
+    hi = bin + 1 < (uint32_t)kBins && vbin(kmax) > bin
+             ? first_key_in_bin_at_least(lo, kmax, bin + 1, vbin) - 1u
+             : kmax;
     if (inbin == need) {
       thr = lo - 1u; // lo >= kmin > 0
       done = true;
@@ -597,8 +589,9 @@ __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, 
   const float hr = key_float(kmax) * 0.5f - h0;
   const float scale = (float)kWaveBins / hr;
   if (hr > 0.f && scale < 3.0e38f) {
+    // one explicit FMA, so every evaluation of a key's bin rounds alike
     auto vbin = [&](uint32_t kk) -> uint32_t {
-      const float x = (key_float(kk) * 0.5f - h0) * scale;
+      const float x = __builtin_fmaf(key_float(kk), 0.5f, -h0) * scale;
       return (uint32_t)fminf(x, (float)(kWaveBins - 1));
     };
     uint32_t bin;
@@ -608,18 +601,11 @@ __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, 
         above, inbin);
     need -= above;
     cand = inbin;
-    uint32_t bmin = 0xFFFFFFFFu, bmax = 0u;
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      uint32_t kk = key[i];
-      asm volatile("" : "+v"(kk)); // recompute the bin rather than keep 64 of them live
-      if (kk != 0u && vbin(kk) == bin) {
-        bmin = kk < bmin ? kk : bmin;
-        bmax = kk > bmax ? kk : bmax;
-      }
-    }
-    lo = wave_reduce_min(bmin); // the bin's keys are exactly those in [lo, hi]
-    hi = wave_reduce_max(bmax);
+    // the bin's keys form the key interval [lo, hi] (see the block kernel)
+    lo = first_key_in_bin_at_least(kmin - 1u, kmax, bin, vbin);
+    hi = bin + 1 < (uint32_t)kWaveBins && vbin(kmax) > bin
+             ? first_key_in_bin_at_least(lo, kmax, bin + 1, vbin) - 1u
+             : kmax;
     if (inbin == need) {
       thr = lo - 1u; // lo >= kmin > 0
       done = true;
