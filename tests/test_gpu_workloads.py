@@ -67,7 +67,8 @@ def _exact_topk_on_oracle_logits(case, rows, ref, E):
 def test_workload1_single_sequence_decode():
     log("workload 1")
     case = synth.workload(1)
-    logits, out, cnt = run_decode(DeviceCase(case))
+    # the launch configuration bench.py times: no schedule buffer (B <= 1024)
+    logits, out, cnt = run_decode(DeviceCase(case), inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     ref, E = _check_sampled(case, logits, out, [0], "w1")
     _exact_topk_on_oracle_logits(case, [0], ref, E)
@@ -78,13 +79,14 @@ def test_workload2_batched_decode_graph_replay():
     case = synth.workload(2)
     dc = DeviceCase(case)
     n_ctas = idx.idx_recommended_ctas(case.R)
-    logits, out, cnt = run_decode(dc, n_ctas=n_ctas)
+    logits, out, cnt = run_decode(dc, n_ctas=n_ctas, inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     rng = np.random.default_rng(2)
     rows = sorted(set([0, case.R - 1] + list(rng.choice(case.R, 6, replace=False))))
     ref, E = _check_sampled(case, logits, out, rows, "w2")
     _exact_topk_on_oracle_logits(case, rows, ref, E)
-    # the same step captured once and replayed gives the same bits
+    # the same step captured once and replayed gives the same bits, with the
+    # schedule buffer as well as without it
     cta = torch.empty(idx.idx_schedule_ints(n_ctas), dtype=torch.int32, device="cuda")
     lg = torch.full_like(logits.cuda(), float("nan"))
     og = torch.empty_like(out.cuda())
@@ -113,7 +115,8 @@ def test_workload2_batched_decode_graph_replay():
 def test_workload3_mtp_decode_page32_padded_rows():
     log("workload 3")
     case = synth.workload(3)
-    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=idx.idx_recommended_ctas(case.R))
+    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=idx.idx_recommended_ctas(case.R),
+                                  inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     rng = np.random.default_rng(3)
     forced = list(range(12))  # both MTP rows of the six edge-length sequences
@@ -159,7 +162,8 @@ def test_workload4_chunked_prefill():
 def test_workload5_mxfp4_decode():
     log("workload 5")
     case = synth.workload(5)
-    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=idx.idx_recommended_ctas(case.R))
+    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=idx.idx_recommended_ctas(case.R),
+                                  inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     rng = np.random.default_rng(5)
     rows = sorted(set([int(np.argmax(case.lens))] + list(rng.choice(case.R, 5, replace=False))))
