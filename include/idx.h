@@ -353,7 +353,9 @@ const char *idx_status_string(idx_status s);
 /* Message of the last failed call on this thread ("" if none). */
 const char *idx_last_error(void);
 
-/* ABI version of this library (major*10000 + minor*100 + patch). */
+/* ABI version of this library (major*10000 + minor*100 + patch). 0.2.0 adds
+ * the K-cache writer, the query quantizer, ragged decode, the prefill
+ * index_base argument, query flags and decode without a schedule buffer. */
 int32_t idx_version(void);
 
 #ifdef __cplusplus
