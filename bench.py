@@ -570,7 +570,7 @@ def main():
         summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(sequences shard across GPUs with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)

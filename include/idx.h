@@ -48,7 +48,7 @@ extern "C" {
 typedef enum idx_status {
     IDX_OK = 0,
     IDX_ERR_INVALID = 1,     /* bad pointer, size, stride or alignment */
-    IDX_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    IDX_ERR_UNSUPPORTED = 2, /* valid request this library does not implement */
     IDX_ERR_WORKSPACE = 3,   /* caller-provided buffer too small */
     IDX_ERR_HIP = 4          /* a HIP runtime call failed */
 } idx_status;
