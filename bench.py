@@ -571,7 +571,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange; see the design notes)",
+              "(decode shards by sequence and prefill by query row, with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
