@@ -77,6 +77,9 @@ def _load():
         lib.orc_quantize_query.restype = i32
         lib.orc_quantize_query.argtypes = [i32, P, i64, i64, i32, i32, P, ctypes.c_float, i32,
                                            P, P, P]
+        lib.orc_sparse_mla.restype = i32
+        lib.orc_sparse_mla.argtypes = [P, i64, i32, i32, P, i64, i64, i32, i64, P, i64, i32, P,
+                                       i64, P, ctypes.c_double, P, P]
         lib.orc_varlen_windows.restype = i32
         lib.orc_varlen_windows.argtypes = [P, P, i32, i64, P]
         lib.orc_varlen_logits.restype = i32
@@ -299,3 +302,24 @@ def varlen_logits(dtype, q, q_scale, w, H, D, cache: Cache, block_tables, lens, 
     if rc != 0:
         raise ValueError("oracle varlen_logits failed with code %d" % rc)
     return out, E
+
+
+def sparse_mla(q, cache_data, page_stride, row_stride, page_size, num_pages, block_tables,
+               next_n, indices, topk_lens, scale):
+    """Sparse attention of bf16 query rows q (uint16 bits [R, H, D]) over the
+    selected latent rows of a bf16 paged cache (uint8 bytes). Returns
+    (out float64 [R, H, D], lse float64 [R, H])."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    R, H, D = q.shape
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    lens = np.ascontiguousarray(topk_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    data = np.ascontiguousarray(cache_data).view(np.uint8)
+    out = np.empty((R, H, D), dtype=np.float64)
+    lse = np.empty((R, H), dtype=np.float64)
+    rc = _load().orc_sparse_mla(_ptr(q), R, H, D, _ptr(data), page_stride, row_stride, page_size,
+                                num_pages, _ptr(bt), bt.shape[1], next_n, _ptr(idx),
+                                idx.shape[1], _ptr(lens), float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle sparse_mla failed with code %d" % rc)
+    return out, lse

@@ -675,3 +675,113 @@ int orc_varlen_logits(int dtype, const uint8_t *q, const uint8_t *q_scale,
     free(Eall);
     return rc_all;
 }
+
+/* ---- Sparse attention over the selected tokens (the consumer of the
+ * top-k: flashinfer PR #3269 "Add DeepSeek V4 sparse MLA TRTLLM-GEN
+ * kernels", summary and review: a decode over dynamic per-row top-k lengths
+ * with 512-dim QK and V, i.e. MLA where the values are the same latent rows
+ * as the keys). Reading (the pages give only the API surface): row r of
+ * sequence b = r / next_n with n = min(topk_lens[r], k) entries of
+ * indices[r][.], entries < 0 skipped; for head h
+ *     s_i = scale * (q[r][h] . c[t_i]),   out[r][h] = sum_i softmax(s)_i c[t_i]
+ * with c[t] the bf16 latent row of sequence-local token t through the block
+ * table; lse[r][h] = log sum_i exp(s_i). No selected token: out = 0,
+ * lse = -inf. Everything in double precision from the bf16 inputs. */
+
+static double orc_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+int orc_sparse_mla(const uint16_t *q, int64_t R, int H, int D,
+                   const uint8_t *kv, int64_t page_stride, int64_t row_stride, int page_size,
+                   int64_t num_pages, const int32_t *block_tables, int64_t bt_stride,
+                   int next_n, const int32_t *indices, int64_t k, const int32_t *topk_lens,
+                   double scale, double *out, double *lse)
+{
+    int64_t r;
+    int rc_all = ORC_OK;
+    if (R < 0 || H < 1 || D < 1 || page_size < 1 || next_n < 1 || k < 0)
+        return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < R; ++r) {
+        const int64_t b = r / next_n;
+        int64_t n = topk_lens[r] < k ? topk_lens[r] : k;
+        double *c = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)D);
+        int64_t *ok = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+        int64_t i, m = 0;
+        int h, d;
+        if (!c || !ok) {
+#pragma omp critical
+            rc_all = ORC_BAD_ARG;
+            free(c);
+            free(ok);
+            continue;
+        }
+        if (n < 0)
+            n = 0;
+        /* gather the selected latent rows */
+        for (i = 0; i < n; ++i) {
+            const int32_t t = indices[r * k + i];
+            int64_t lp, pg;
+            const uint8_t *row;
+            if (t < 0)
+                continue;
+            lp = t / page_size;
+            if (lp >= bt_stride) {
+#pragma omp critical
+                rc_all = ORC_BAD_PAGE;
+                continue;
+            }
+            pg = block_tables[b * bt_stride + lp];
+            if (pg < 0 || pg >= num_pages) {
+#pragma omp critical
+                rc_all = ORC_BAD_PAGE;
+                continue;
+            }
+            row = kv + pg * page_stride + (int64_t)(t % page_size) * row_stride;
+            for (d = 0; d < D; ++d) {
+                uint16_t v;
+                memcpy(&v, row + 2 * d, 2);
+                c[m * D + d] = orc_bf16(v);
+            }
+            ok[m++] = i;
+        }
+        for (h = 0; h < H; ++h) {
+            const uint16_t *qh = q + (r * H + h) * (int64_t)D;
+            double *o = out + (r * H + h) * (int64_t)D;
+            double mx = -INFINITY, sum = 0.0;
+            double *s = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+            for (d = 0; d < D; ++d)
+                o[d] = 0.0;
+            if (!s) {
+#pragma omp critical
+                rc_all = ORC_BAD_ARG;
+                continue;
+            }
+            for (i = 0; i < m; ++i) {
+                double acc = 0.0;
+                for (d = 0; d < D; ++d)
+                    acc += orc_bf16(qh[d]) * c[i * D + d];
+                s[i] = scale * acc;
+                mx = s[i] > mx ? s[i] : mx;
+            }
+            for (i = 0; i < m; ++i)
+                sum += exp(s[i] - mx);
+            for (i = 0; i < m; ++i) {
+                const double p = exp(s[i] - mx) / sum;
+                for (d = 0; d < D; ++d)
+                    o[d] += p * c[i * D + d];
+            }
+            if (lse)
+                lse[r * H + h] = m > 0 ? mx + log(sum) : -INFINITY;
+            free(s);
+        }
+        free(c);
+        free(ok);
+    }
+    return rc_all;
+}

@@ -418,3 +418,83 @@ def ragged_offsets(rng, B, max_q, forced=(0, 1)):
     off = np.zeros(B + 1, dtype=np.int32)
     off[1:] = np.cumsum(n)
     return off
+
+
+# ---------------------------------------------------- sparse MLA over top-k
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass
+class MlaCase:
+    """Sparse attention inputs: bf16 latent rows (D values) in pages of P
+    rows, query rows (bits, [R, H, D]), per-row selected token lists."""
+    q: np.ndarray            # uint16 [R, H, D]
+    data: np.ndarray         # uint8 pool, num_pages * page_stride bytes
+    page_stride: int
+    row_stride: int
+    page_size: int
+    num_pages: int
+    block_tables: np.ndarray # int32 [B, bt_stride]
+    lens: np.ndarray         # int32 [B] context lengths
+    next_n: int
+    indices: np.ndarray      # int32 [R, k], -1 past each row's count
+    topk_lens: np.ndarray    # int32 [R]
+    k: int
+    H: int = 64
+    D: int = 512
+
+    @property
+    def R(self):
+        return int(self.q.shape[0])
+
+
+def mla_case(lens, *, next_n=1, P=64, k=2048, H=64, D=512, row_stride=None, seed=0,
+             full=False, holes=False):
+    """Selected lists: each row picks min(k, E_r) distinct tokens of its
+    visible window (E_r as in decode) in random order, or every visible token
+    when full; holes sets a few entries inside the count to -1."""
+    rng = rng_for(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    B = len(lens)
+    row_stride = row_stride or 2 * D
+    npg = (lens + P - 1) // P
+    pool = max(int(npg.sum()) + 3, 1)
+    perm = rng.permutation(pool).astype(np.int64)
+    bt_w = max(int(npg.max()) if B else 1, 1)
+    bt = np.full((B, bt_w), BT_SENTINEL, dtype=np.int32)
+    data = np.zeros(pool * P * row_stride, dtype=np.uint8)
+    used = 0
+    for b in range(B):
+        n = int(npg[b])
+        pages = perm[used:used + n]
+        used += n
+        bt[b, :n] = pages
+        L = int(lens[b])
+        if L == 0:
+            continue
+        rows = (pages[:, None] * P + np.arange(P)[None, :]).reshape(-1)[:L]
+        vals = rng.standard_normal((L, D), dtype=np.float32)
+        bits = _bf16_bits(vals).view(np.uint8).reshape(L, 2 * D)
+        view = data.reshape(pool * P, row_stride)
+        view[rows, :2 * D] = bits
+    R = B * next_n
+    q = _bf16_bits(rng.standard_normal((R, H, D), dtype=np.float32) / np.float32(8.0))
+    idx = np.full((R, k), -1, dtype=np.int32)
+    tl = np.zeros(R, dtype=np.int32)
+    for r in range(R):
+        b, j = divmod(r, next_n)
+        E = max(0, int(lens[b]) - (next_n - 1 - j))
+        n = min(k, E)
+        sel = np.arange(E) if full else rng.permutation(E)[:n]
+        if not full:
+            idx[r, :n] = sel
+        else:
+            idx[r, :n] = sel[:n]
+        if holes and n > 4:
+            idx[r, rng.integers(0, n, size=3)] = -1
+        tl[r] = n
+    return MlaCase(q, data, P * row_stride, row_stride, P, pool, bt, lens.astype(np.int32),
+                   next_n, idx, tl, k, H, D)

@@ -646,3 +646,70 @@ def test_varlen_rows_match_dense_formulation():
         scale = max(np.abs(ref).max() if e else 1.0, 1e-30)
         assert np.max(np.abs(got[r, :e] - ref), initial=0.0) <= 1e-12 * scale
         assert np.all(np.isneginf(got[r, e:]))
+
+
+# ------------------------------------------- sparse attention over top-k
+
+def _mla(case, scale):
+    return oracle.sparse_mla(case.q, case.data, case.page_stride, case.row_stride,
+                             case.page_size, case.num_pages, case.block_tables, case.next_n,
+                             case.indices, case.topk_lens, scale)
+
+
+def _mla_rows(case, b, tokens):
+    """Latent rows of sequence b's tokens, decoded by torch from the pool."""
+    P = case.page_size
+    pages = case.block_tables[b, np.asarray(tokens) // P].astype(np.int64)
+    rows = pages * P + np.asarray(tokens) % P
+    raw = case.data.reshape(-1, case.row_stride)[rows, :2 * case.D]
+    bits = np.ascontiguousarray(raw).view(np.int16)
+    return torch.from_numpy(bits).view(torch.bfloat16).double().numpy()
+
+
+def _q64(case, r):
+    return torch.from_numpy(case.q[r].view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def test_sparse_mla_single_token_returns_its_row_and_scale_zero_the_mean():
+    """One selected token: the softmax weight is 1 and every head returns
+    that latent row; scale 0: uniform weights, the mean of the rows."""
+    case = synth.mla_case([40, 70], next_n=1, P=32, k=8, D=64, H=4, seed=61)
+    case.topk_lens[0] = 1
+    out, lse = _mla(case, 0.3)
+    c = _mla_rows(case, 0, [case.indices[0, 0]])
+    assert np.array_equal(out[0], np.repeat(c, 4, axis=0))
+    out0, lse0 = _mla(case, 0.0)
+    mean = _mla_rows(case, 1, case.indices[1, :8]).mean(axis=0)
+    assert np.allclose(out0[1], mean[None, :], rtol=0, atol=1e-12)
+    assert np.allclose(lse0[1], np.log(8.0))
+
+
+def test_sparse_mla_matches_dense_softmax_and_ignores_list_order():
+    """Against torch float64 softmax(scale q c^T) c on the gathered rows, and
+    the same result for a permuted selection list; skipped (-1) entries and
+    an empty row (zeros, lse -inf)."""
+    case = synth.mla_case([300, 0, 129], next_n=2, P=64, k=64, D=128, H=8, seed=62,
+                          holes=True)
+    scale = 0.07
+    out, lse = _mla(case, scale)
+    for r in range(case.R):
+        b = r // 2
+        n = int(case.topk_lens[r])
+        sel = case.indices[r, :n]
+        sel = sel[sel >= 0]
+        if len(sel) == 0:
+            assert np.all(out[r] == 0) and np.all(np.isneginf(lse[r]))
+            continue
+        c = torch.from_numpy(_mla_rows(case, b, sel))
+        qd = torch.from_numpy(_q64(case, r))
+        s = scale * (qd @ c.T)
+        ref = torch.softmax(s, dim=1) @ c
+        assert np.allclose(out[r], ref.numpy(), rtol=0, atol=1e-10)
+        assert np.allclose(lse[r], torch.logsumexp(s, dim=1).numpy(), atol=1e-10)
+    perm = case.indices.copy()
+    for r in range(case.R):
+        n = int(case.topk_lens[r])
+        perm[r, :n] = np.random.default_rng(r).permutation(perm[r, :n])
+    case.indices = perm
+    out2, _ = _mla(case, scale)
+    assert np.allclose(out2, out, rtol=0, atol=1e-12)
