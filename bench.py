@@ -500,6 +500,51 @@ def q_quant_bench(args, torch, idx, R_decode):
                         "folded into the weights", "runs": res}
 
 
+def sparse_mla_bench(args, torch, idx, synth):
+    """Sparse attention over the decode batch's selection: 64 rows, 2048
+    listed tokens each (512-dim bf16 latent rows, page 64), 64 heads."""
+    import numpy as np
+    rng = np.random.default_rng(9)
+    lens = rng.integers(2048, 32768 + 1, size=64)
+    case = synth.mla_case(lens, next_n=1, P=64, k=2048, seed=10)
+    R, k = case.R, case.k
+    q = torch.from_numpy(case.q.view(np.int16)).cuda()
+    data = torch.from_numpy(case.data).cuda()
+    bt = torch.from_numpy(case.block_tables).cuda()
+    ind = torch.from_numpy(case.indices).cuda()
+    tl = torch.from_numpy(case.topk_lens).cuda()
+    out = torch.empty((R, 64, 512), dtype=torch.int16, device="cuda")
+    lse = torch.empty((R, 64), dtype=torch.float32, device="cuda")
+    wsb = idx.idx_sparse_mla_workspace_size(R, k)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
+    kv = idx.make_mla_cache(case.page_size, case.num_pages, data, case.page_stride,
+                            case.row_stride)
+
+    def call():
+        idx.idx_sparse_mla_decode(q, kv, bt, case.block_tables.shape[1], R, 1, ind, tl, k, 0.0442,
+                                  out, lse, ws, wsb)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    n = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    listed = int(case.topk_lens.sum())
+    nbytes = listed * 1024 + R * 64 * 512 * 2 * 2 + R * k * 4  # rows, q + out, lists
+    flops = 2.0 * 2 * listed * 64 * 512
+    return {"workload": "sparse attention over the selection: 64 rows x 2048 listed tokens, "
+                        "64 heads, 512-dim bf16 latent rows, page 64",
+            "us_per_call": ms * 1e3, "algorithmic_bytes": nbytes,
+            "achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "bf16_tflops": flops / (ms * 1e-3) / 1e12,
+            "workspace_bytes": wsb}
+
+
 def cpu_baseline(case, budget_s):
     """The CPU oracle on a bounded sample of the decode workload: groups of
     rows in a fixed random order, cycling over the workload's rows, until
@@ -614,6 +659,11 @@ def main():
         for r in qq["runs"]:
             log("query quantization: %.1f us per %d rows, %.0f GB/s" % (
                 r["us_per_call"], r["rows"], r["achieved_gbs"]))
+    mla = None
+    if not args.no_prefill:
+        mla = sparse_mla_bench(args, torch, idx, synth)
+        log("sparse attention: %.1f us per call, %.0f GB/s, %.1f TFLOP/s bf16" % (
+            mla["us_per_call"], mla["achieved_gbs"], mla["bf16_tflops"]))
     others = []
     if args.all_workloads:
         for wl in (1, 3, 5):
@@ -692,6 +742,8 @@ def main():
         line["kv_cache_write"] = kvw
     if qq:
         line["query_quantization"] = qq
+    if mla:
+        line["sparse_attention"] = mla
     if others:
         line["other_decode_workloads"] = others
     print(json.dumps(line), flush=True)

@@ -347,6 +347,49 @@ idx_status idx_kv_cache_write(const void *k, int32_t k_dtype, int64_t k_row_stri
 idx_status idx_quantize_query(const void *x, int32_t x_dtype, int64_t x_row_stride, int32_t R,
                               const float *w, float c, const idx_query *out, void *stream);
 
+/* Paged cache of bf16 latent rows (512 values) for the sparse attention:
+ * token slot s of physical page p at data + p*page_stride_bytes +
+ * s*row_stride_bytes. data 16-byte aligned; strides multiples of 16;
+ * row_stride_bytes >= 1024; page_stride_bytes >= page_size*row_stride_bytes. */
+typedef struct idx_mla_cache {
+    int32_t page_size; /* 32, 64 or 256 */
+    int32_t reserved;  /* set to 0 */
+    int64_t num_pages;
+    const void *data;
+    int64_t page_stride_bytes;
+    int64_t row_stride_bytes;
+} idx_mla_cache;
+
+/* Workspace bytes idx_sparse_mla_decode needs for R rows and lists of k. */
+size_t idx_sparse_mla_workspace_size(int32_t R, int32_t k);
+
+/*
+ * Sparse attention over the indexer's selection (the consumer of the top-k:
+ * flashinfer PR #3269 "Add DeepSeek V4 sparse MLA TRTLLM-GEN kernels", a
+ * decode over dynamic per-row top-k lengths with 512-dim QK and V; the
+ * values are the latent rows themselves). Row r = b*next_n + j:
+ *   n_r = min(topk_lens[r], k) entries of indices[r*k ..] (sequence-local
+ *   token ids, e.g. idx_topk's output and counts; entries < 0 are skipped),
+ *   s_i = scale * (q[r][h] . c[t_i]),  out[r][h] = sum_i softmax(s)_i c[t_i],
+ *   lse[r][h] = log sum_i exp(s_i); no listed token: out = 0, lse = -inf.
+ *   q     bf16 [R][64][512], 16-byte aligned
+ *   kv    the latent cache; c[t] is slot t % P of page block_tables[b][t / P]
+ *   out   bf16 [R][64][512] (written), 8-byte aligned
+ *   lse   fp32 [R][64] or NULL
+ *   ws    at least idx_sparse_mla_workspace_size(R, k) bytes, 16-byte aligned
+ * Listed tokens must lie inside the sequence's pages (device contract, not
+ * checked); a table entry outside the pool reads a zero row instead of
+ * faulting. Arithmetic: bf16 products with fp32 accumulation, probabilities
+ * rounded to bf16 for the P.V product, fp32 softmax, bf16 output.
+ * Errors: IDX_ERR_INVALID (null pointers, shapes, strides, alignment, scale
+ * not finite, B*next_n > 65535), IDX_ERR_WORKSPACE (ws too small).
+ */
+idx_status idx_sparse_mla_decode(const void *q, const idx_mla_cache *kv,
+                                 const int32_t *block_tables, int64_t bt_stride, int32_t B,
+                                 int32_t next_n, const int32_t *indices,
+                                 const int32_t *topk_lens, int32_t k, float scale, void *out,
+                                 float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable name of a status (static string). */
 const char *idx_status_string(idx_status s);
 

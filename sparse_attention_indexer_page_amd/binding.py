@@ -34,8 +34,15 @@ EXPORTS = (
     "idx_topk_workspace_size", "idx_topk",
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
     "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_kv_cache_write",
-    "idx_quantize_query", "idx_status_string", "idx_last_error", "idx_version",
+    "idx_quantize_query", "idx_sparse_mla_workspace_size", "idx_sparse_mla_decode",
+    "idx_status_string", "idx_last_error", "idx_version",
 )
+
+
+class MlaCache(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("data", ctypes.c_void_p),
+                ("page_stride_bytes", ctypes.c_int64), ("row_stride_bytes", ctypes.c_int64)]
 
 
 class IdxError(RuntimeError):
@@ -99,6 +106,9 @@ def load(path: str = LIB_PATH):
         "idx_kv_cache_write": (st, [P, i32, i64, i32, P, ctypes.POINTER(KVCache), P]),
         "idx_quantize_query": (st, [P, i32, i64, i32, P, ctypes.c_float,
                                     ctypes.POINTER(Query), P]),
+        "idx_sparse_mla_workspace_size": (sz, [i32, i32]),
+        "idx_sparse_mla_decode": (st, [P, ctypes.POINTER(MlaCache), P, i64, i32, i32, P, P, i32,
+                                       ctypes.c_float, P, P, P, sz, P]),
         "idx_status_string": (ctypes.c_char_p, [st]),
         "idx_last_error": (ctypes.c_char_p, []),
         "idx_version": (i32, []),
@@ -245,3 +255,20 @@ def idx_varlen_windows(context_lens, row_offsets, B, max_q, visible_end, stream=
     _check(load().idx_varlen_windows(ptr(context_lens), ptr(row_offsets), B, max_q,
                                      ptr(visible_end), stream_handle(stream)),
            "idx_varlen_windows")
+
+
+def make_mla_cache(page_size, num_pages, data, page_stride_bytes, row_stride_bytes) -> MlaCache:
+    return MlaCache(page_size, 0, num_pages, ptr(data), page_stride_bytes, row_stride_bytes)
+
+
+def idx_sparse_mla_workspace_size(R, k) -> int:
+    return load().idx_sparse_mla_workspace_size(R, k)
+
+
+def idx_sparse_mla_decode(q, kv: MlaCache, block_tables, bt_stride, B, next_n, indices,
+                          topk_lens, k, scale, out, lse, ws, ws_bytes, stream=None):
+    _check(load().idx_sparse_mla_decode(ptr(q), ctypes.byref(kv), ptr(block_tables), bt_stride,
+                                        B, next_n, ptr(indices), ptr(topk_lens), k, scale,
+                                        ptr(out), ptr(lse), ptr(ws), ws_bytes,
+                                        stream_handle(stream)),
+           "idx_sparse_mla_decode")

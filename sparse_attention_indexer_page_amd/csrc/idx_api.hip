@@ -384,6 +384,82 @@ idx_status idx_quantize_query(const void *x, int32_t x_dtype, int64_t x_row_stri
   return ok();
 }
 
+namespace {
+
+// Chunks per row of the sparse attention: enough work groups to cover the
+// chip (R * nsplit >= 256), chunks of at least 64 listed entries.
+void mla_split(int32_t R, int32_t k, int32_t *nsplit, int32_t *chunk) {
+  int32_t ns = R >= 256 ? 1 : (256 + R - 1) / R;
+  const int32_t max_ns = (k + 63) / 64;
+  ns = ns < max_ns ? ns : max_ns;
+  ns = ns < 1 ? 1 : ns;
+  int32_t ch = (k + ns - 1) / ns;
+  ch = (ch + 15) / 16 * 16;
+  *nsplit = (k + ch - 1) / ch;
+  *chunk = ch;
+}
+
+} // namespace
+
+size_t idx_sparse_mla_workspace_size(int32_t R, int32_t k) {
+  if (R < 1 || k < 1) return 0;
+  int32_t ns, ch;
+  mla_split(R, k, &ns, &ch);
+  return (size_t)R * ns * 64 * (512 + 2) * sizeof(float);
+}
+
+idx_status idx_sparse_mla_decode(const void *q, const idx_mla_cache *kv,
+                                 const int32_t *block_tables, int64_t bt_stride, int32_t B,
+                                 int32_t next_n, const int32_t *indices,
+                                 const int32_t *topk_lens, int32_t k, float scale, void *out,
+                                 float *lse, void *ws, size_t ws_bytes, void *stream) {
+  if (!q || !kv || !block_tables || !indices || !topk_lens || !out || !ws)
+    return fail(IDX_ERR_INVALID, "null q, kv, block_tables, indices, topk_lens, out or ws");
+  if (!valid_page_size(kv->page_size))
+    return fail(IDX_ERR_INVALID, "page_size %d not in {32, 64, 256}", kv->page_size);
+  if (!kv->data || kv->num_pages < 1) return fail(IDX_ERR_INVALID, "empty latent cache");
+  if (!aligned(kv->data, 16) || kv->page_stride_bytes % 16 || kv->row_stride_bytes % 16 ||
+      kv->row_stride_bytes < 1024 ||
+      kv->page_stride_bytes < (int64_t)kv->page_size * kv->row_stride_bytes)
+    return fail(IDX_ERR_INVALID, "latent cache rows must be >= 1024 B, strides multiples of 16");
+  if (B < 1) return fail(IDX_ERR_INVALID, "B must be >= 1");
+  if (next_n < 1 || next_n > 4) return fail(IDX_ERR_INVALID, "next_n = %d outside [1, 4]", next_n);
+  if ((int64_t)B * next_n > 65535) return fail(IDX_ERR_INVALID, "too many rows");
+  if (bt_stride < 1) return fail(IDX_ERR_INVALID, "bt_stride must be >= 1");
+  if (k < 1) return fail(IDX_ERR_INVALID, "k = %d must be >= 1", k);
+  if (!std::isfinite(scale)) return fail(IDX_ERR_INVALID, "scale is not finite");
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(ws, 16) || (lse && !aligned(lse, 4)))
+    return fail(IDX_ERR_INVALID, "q (16 B), out (8 B), ws (16 B) or lse misaligned");
+  const int32_t R = B * next_n;
+  if (ws_bytes < idx_sparse_mla_workspace_size(R, k))
+    return fail(IDX_ERR_WORKSPACE, "workspace %zu B < %zu B", ws_bytes,
+                idx_sparse_mla_workspace_size(R, k));
+  idx::MlaArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.kv = static_cast<const uint8_t *>(kv->data);
+  a.page_stride = kv->page_stride_bytes;
+  a.row_stride = kv->row_stride_bytes;
+  a.page_size = kv->page_size;
+  a.page_shift = kv->page_size == 32 ? 5 : (kv->page_size == 64 ? 6 : 8);
+  a.num_pages = kv->num_pages;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.next_n = next_n;
+  a.R = R;
+  a.indices = indices;
+  a.k = k;
+  a.topk_lens = topk_lens;
+  a.scale = scale;
+  mla_split(R, k, &a.nsplit, &a.chunk);
+  a.ws_o = static_cast<float *>(ws);
+  a.ws_ml = a.ws_o + (size_t)R * a.nsplit * 64 * 512;
+  a.out = static_cast<uint16_t *>(out);
+  a.lse = lse;
+  hipError_t e = idx::launch_sparse_mla(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+  return ok();
+}
+
 int64_t idx_prefill_rows_per_chunk(int64_t W, int64_t budget_bytes) {
   if (W < 1) return 0;
   return prefill_rows_per_chunk(W, budget_bytes);

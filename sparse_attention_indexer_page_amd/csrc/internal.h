@@ -118,7 +118,32 @@ struct QQuantArgs {
   float *w_out;         // [R][64]
 };
 
+struct MlaArgs {
+  const uint16_t *q;  // bf16 [R][64][512]
+  const uint8_t *kv;  // bf16 latent rows of 512
+  int64_t page_stride;
+  int64_t row_stride;
+  int32_t page_size;
+  int32_t page_shift;
+  int64_t num_pages;
+  const int32_t *block_tables;
+  int64_t bt_stride;
+  int32_t next_n;
+  int32_t R;
+  const int32_t *indices; // [R][k]
+  int32_t k;
+  const int32_t *topk_lens; // [R]
+  float scale;
+  int32_t nsplit; // chunks per row
+  int32_t chunk;  // listed entries per chunk, a multiple of 16
+  float *ws_o;    // [R][nsplit][64][512]
+  float *ws_ml;   // [R][nsplit][64][2]
+  uint16_t *out;  // bf16 [R][64][512]
+  float *lse;     // [R][64] or null
+};
+
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t s);
 hipError_t launch_fill_tail(const int32_t *lens, const int32_t *row_offsets, int32_t B, int32_t n,
                             int64_t W, float *logits, hipStream_t s);

@@ -282,3 +282,23 @@ def test_logits_rejects_unknown_query_flags(lib, flags):
     q = binding.Query(1, 64, 128, flags, 0x1000, 0x2000, 0x3000)
     assert _logits(q, _kv()) == idx.IDX_ERR_INVALID
     assert "flags" in idx.idx_last_error_message()
+
+
+def test_sparse_mla_rejects_bad_arguments(lib):
+    L = idx.load()
+    kv = idx.MlaCache(64, 0, 10, 0x10000, 64 * 1024, 1024)
+    def call(q=0x1000, kv=kv, bt=0x2000, bts=8, B=2, n=1, ind=0x3000, tl=0x4000, k=16, scale=0.1,
+             out=0x5000, lse=0, ws=0x6000, wsb=1 << 30):
+        return L.idx_sparse_mla_decode(q, ctypes.byref(kv), bt, bts, B, n, ind, tl, k, scale, out,
+                                       lse, ws, wsb, None)
+    assert call(q=0) == idx.IDX_ERR_INVALID
+    assert call(kv=idx.MlaCache(48, 0, 10, 0x10000, 64 * 1024, 1024)) == idx.IDX_ERR_INVALID
+    assert call(kv=idx.MlaCache(64, 0, 10, 0x10000, 64 * 1024, 1008)) == idx.IDX_ERR_INVALID
+    assert call(kv=idx.MlaCache(64, 0, 10, 0x10000, 1024, 1024)) == idx.IDX_ERR_INVALID
+    assert call(n=5) == idx.IDX_ERR_INVALID
+    assert call(k=0) == idx.IDX_ERR_INVALID
+    assert call(scale=float("inf")) == idx.IDX_ERR_INVALID
+    assert call(q=0x1008) == idx.IDX_ERR_INVALID
+    assert call(wsb=16) == idx.IDX_ERR_WORKSPACE
+    assert idx.idx_sparse_mla_workspace_size(2, 16) == 2 * 1 * 64 * 514 * 4
+    assert idx.idx_sparse_mla_workspace_size(0, 16) == 0
