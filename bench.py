@@ -11,9 +11,10 @@ Each step reads its keys from one of several copies of the page pool in
 rotation, so the data a step reads was last touched several steps earlier
 (more than the 256 MiB last-level cache ago): the timed region reads keys from
 HBM, not from the cache. The scoring kernel's average duration comes from a second pass of
-eager launches of the same kernel over the same pool rotation, each bracketed
-by events on its launch stream (rocprofv3's kernel trace of this command
-reports the same kernel's average for cross-checking).
+K eager back-to-back launches of the same kernel over the same pool rotation,
+between two events on its launch stream (rocprofv3's kernel trace of this
+command reports the same kernel's average for cross-checking); a third pass
+brackets each launch with its own events for the per-launch minimum.
 
 Also reported: the chunked-prefill workload (16384 rows over 4096 committed
 keys, causal (r+1)//4, budget 256e6 B, top-2048) as whole-call time, and the
@@ -138,21 +139,34 @@ def decode_bench(args, torch, idx, synth, wl=2, split=None):
     step_ms = (t1 - t0) * 1e3 / K
 
     # Scoring kernel alone: eager launches on the same stream, same pools in
-    # rotation, each bracketed by events. A sleep kernel first lets the host
-    # queue ahead so no event waits on a launch that has not been submitted.
+    # rotation. The average is K back-to-back launches between one pair of
+    # events (kernel time plus the dispatch gap, as a kernel trace sees it);
+    # the per-launch figures bracket each launch with its own events, which
+    # adds the events' own overhead to every launch. A sleep kernel first lets
+    # the host queue ahead so no event waits on a launch not yet submitted.
+    def host_ahead():
+        try:
+            torch.cuda._sleep(2_000_000)
+        except Exception:
+            torch.empty(1 << 28, dtype=torch.uint8, device="cuda").zero_()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    host_ahead()
+    e0.record()
+    for j in range(K):
+        scores(kvs[j % n_sets])
+    e1.record()
+    torch.cuda.synchronize()
+    kern_avg_ms = e0.elapsed_time(e1) / K
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
-    try:
-        torch.cuda._sleep(2_000_000)
-    except Exception:
-        torch.empty(1 << 28, dtype=torch.uint8, device="cuda").zero_()
+    host_ahead()
     for j in range(K):
         kev[j][0].record()
         scores(kvs[j % n_sets])
         kev[j][1].record()
     torch.cuda.synchronize()
     kern_ms = [a.elapsed_time(b) for a, b in kev]
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
 
     lens = case.lens.astype(int)
     E = [max(0, int(l) - (case.next_n - 1 - j)) for l in lens for j in range(case.next_n)]
@@ -339,6 +353,47 @@ def prefill_source_digest():
     return h.hexdigest()[:16]
 
 
+def summarize_trace(trace_dir, out_md, title, command, scoring_groups=None):
+    """A kernel-trace summary (rocprofv3 --kernel-trace --stats, csv) as
+    markdown: per-kernel calls and durations, and, when scoring_groups is
+    given as [(label, first, count), ...], the average duration of those
+    dispatches of the decode scoring kernel in launch order."""
+    import csv
+    import glob
+
+    def rows(pattern):
+        files = glob.glob(os.path.join(trace_dir, "**", pattern), recursive=True)
+        if not files:
+            raise SystemExit("no %s under %s" % (pattern, trace_dir))
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    def short(name):
+        name = name.replace("void ", "").replace("idx::(anonymous namespace)::", "")
+        return name if len(name) <= 72 else name[:69] + "..."
+
+    stats = rows("*kernel_stats.csv")
+    lines = ["# " + title, "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %s |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    if scoring_groups:
+        trace = rows("*kernel_trace.csv")
+        sc = [int(t["End_Timestamp"]) - int(t["Start_Timestamp"]) for t in trace
+              if "mqa_logits_kernel" in t["Kernel_Name"]]
+        lines += ["", "Decode scoring dispatches in launch order, grouped as bench.py issues them:", "",
+                  "| group | dispatches | avg us |", "|---|---|---|"]
+        for label, first, count in scoring_groups:
+            part = sc[first:first + count]
+            if part:
+                lines.append("| %s | %d | %.2f |" % (label, len(part), sum(part) / len(part) / 1e3))
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log("wrote " + out_md)
+
+
 def summarize_mfma(pmc_dir):
     """MFMA use of the prefill scoring kernel from one rocprofv3 run with
     --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
@@ -502,7 +557,10 @@ def q_quant_bench(args, torch, idx, R_decode):
 
 def sparse_mla_bench(args, torch, idx, synth):
     """Sparse attention over the decode batch's selection: 64 rows, 2048
-    listed tokens each (512-dim bf16 latent rows, page 64), 64 heads."""
+    listed tokens each (512-dim bf16 latent rows, page 64), 64 heads. Calls
+    rotate over four copies of the latent cache (each call's 134 MB of rows
+    was last touched three calls earlier, beyond the 256 MiB last-level
+    cache), timed back to back between two events."""
     import numpy as np
     rng = np.random.default_rng(9)
     lens = rng.integers(2048, 32768 + 1, size=64)
@@ -510,6 +568,7 @@ def sparse_mla_bench(args, torch, idx, synth):
     R, k = case.R, case.k
     q = torch.from_numpy(case.q.view(np.int16)).cuda()
     data = torch.from_numpy(case.data).cuda()
+    copies = [data] + [data.clone() for _ in range(3)]
     bt = torch.from_numpy(case.block_tables).cuda()
     ind = torch.from_numpy(case.indices).cuda()
     tl = torch.from_numpy(case.topk_lens).cuda()
@@ -517,32 +576,33 @@ def sparse_mla_bench(args, torch, idx, synth):
     lse = torch.empty((R, 64), dtype=torch.float32, device="cuda")
     wsb = idx.idx_sparse_mla_workspace_size(R, k)
     ws = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
-    kv = idx.make_mla_cache(case.page_size, case.num_pages, data, case.page_stride,
-                            case.row_stride)
+    kvs = [idx.make_mla_cache(case.page_size, case.num_pages, d, case.page_stride,
+                              case.row_stride) for d in copies]
 
-    def call():
-        idx.idx_sparse_mla_decode(q, kv, bt, case.block_tables.shape[1], R, 1, ind, tl, k, 0.0442,
-                                  out, lse, ws, wsb)
+    def call(j):
+        idx.idx_sparse_mla_decode(q, kvs[j % len(kvs)], bt, case.block_tables.shape[1], R, 1, ind,
+                                  tl, k, 0.0442, out, lse, ws, wsb)
 
-    for _ in range(3):
-        call()
+    for j in range(4):
+        call(j)
     torch.cuda.synchronize()
     n = 20
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(n):
-        call()
+    for j in range(n):
+        call(j)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     listed = int(case.topk_lens.sum())
     nbytes = listed * 1024 + R * 64 * 512 * 2 * 2 + R * k * 4  # rows, q + out, lists
     flops = 2.0 * 2 * listed * 64 * 512
+    gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "sparse attention over the selection: 64 rows x 2048 listed tokens, "
                         "64 heads, 512-dim bf16 latent rows, page 64",
             "us_per_call": ms * 1e3, "algorithmic_bytes": nbytes,
-            "achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "bf16_tflops": flops / (ms * 1e-3) / 1e12,
-            "workspace_bytes": wsb}
+            "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "bf16_tflops": flops / (ms * 1e-3) / 1e12, "workspace_bytes": wsb}
 
 
 def cpu_baseline(case, budget_s):
@@ -603,13 +663,48 @@ def main():
                     help="write the profiles/ MFMA summary from a --prefill-counters PMC run")
     ap.add_argument("--counters", action="store_true",
                     help="only a reference copy + scoring launches, for rocprofv3 --pmc runs")
+    ap.add_argument("--sparse-attention-only", action="store_true",
+                    help="time only the sparse attention over the selection (one JSON line)")
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time the other decode workloads (single sequence, MTP page 32, MXFP4)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write the profiles/ kernel-trace summary of a --kernel-trace --stats run")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ traffic summary from two --counters PMC runs")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        d = args.summarize_trace
+        if args.sparse_attention_only:
+            summarize_trace(d, os.path.join(ROOT, "profiles", "sparse_mla_decode_64x2048_kernel_trace.md"),
+                            "Kernel trace of the sparse attention over the selection: 64 rows x 2048 "
+                            "listed tokens, 64 heads, 512-dim bf16 latent rows, page 64",
+                            "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                            "python3 -u bench.py --sparse-attention-only\n"
+                            "python3 bench.py --sparse-attention-only --summarize-trace <dir>")
+        else:
+            # per decode run: 4 eager steps, warmup replays, timed replays,
+            # back-to-back eager launches, bracketed eager launches
+            n, w = args.steps, args.warmup
+            groups = []
+            for i, run in enumerate(("in-kernel split", "schedule buffer")):
+                base = i * (4 + w + 3 * n)
+                groups += [(run + ": timed graph replays", base + 4 + w, n),
+                           (run + ": back-to-back eager launches (the bench's average)",
+                            base + 4 + w + n, n),
+                           (run + ": eager launches, each bracketed by events",
+                            base + 4 + w + 2 * n, n)]
+            summarize_trace(d, os.path.join(ROOT, "profiles", "kernels_decode_batched_and_prefill_chunked.md"),
+                            "Kernel trace of bench.py: batched decode (64 seqs, FP8, page 64, top-2048, "
+                            "graph replay; with and without the schedule buffer), chunked prefill (16384 "
+                            "rows x 4096 keys, 2 chunks), K-cache write, query quantization, sparse "
+                            "attention",
+                            "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                            "python3 -u bench.py --steps %d --warmup %d --no-cpu-baseline\n"
+                            "python3 bench.py --steps %d --warmup %d --summarize-trace <dir>" % (n, w, n, w),
+                            groups)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
@@ -636,6 +731,9 @@ def main():
         return
     if args.prefill_counters:
         prefill_counter_run(args, torch, idx, synth)
+        return
+    if args.sparse_attention_only:
+        print(json.dumps(sparse_mla_bench(args, torch, idx, synth)), flush=True)
         return
     d = decode_bench(args, torch, idx, synth)
     log("decode (%s split): step %.3f ms, scoring kernel %.3f ms avg (%.3f min), %.0f GB/s" % (
@@ -711,6 +809,7 @@ def main():
             "traffic": d["traffic"],
             "kernel": "mqa_logits_kernel<FP8, 1 row>",
             "kernel_avg_us": d["kern_avg_ms"] * 1e3,
+            "kernel_min_us_bracketed": d["kern_min_ms"] * 1e3,
             "algorithmic_bytes_per_launch": d["launch_bytes"],
         },
         "cpu_baseline": cpu,

@@ -387,14 +387,17 @@ idx_status idx_quantize_query(const void *x, int32_t x_dtype, int64_t x_row_stri
 namespace {
 
 // Chunks per row of the sparse attention: enough work groups to cover the
-// chip (R * nsplit >= 256), chunks of at least 64 listed entries.
+// chip (R * nsplit >= 256) with chunks of at least 64 listed entries, and
+// never more than kMlaMaxChunk entries per chunk (the kernel's LDS table).
 void mla_split(int32_t R, int32_t k, int32_t *nsplit, int32_t *chunk) {
   int32_t ns = R >= 256 ? 1 : (256 + R - 1) / R;
   const int32_t max_ns = (k + 63) / 64;
   ns = ns < max_ns ? ns : max_ns;
+  const int32_t min_ns = (k + idx::kMlaMaxChunk - 1) / idx::kMlaMaxChunk;
+  ns = ns > min_ns ? ns : min_ns;
   ns = ns < 1 ? 1 : ns;
   int32_t ch = (k + ns - 1) / ns;
-  ch = (ch + 15) / 16 * 16;
+  ch = (ch + 15) / 16 * 16; // <= kMlaMaxChunk, a multiple of 16
   *nsplit = (k + ch - 1) / ch;
   *chunk = ch;
 }

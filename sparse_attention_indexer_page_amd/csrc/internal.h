@@ -118,6 +118,10 @@ struct QQuantArgs {
   float *w_out;         // [R][64]
 };
 
+// Listed entries one sparse-attention work group takes (its table of row
+// addresses lives in LDS).
+constexpr int kMlaMaxChunk = 512;
+
 struct MlaArgs {
   const uint16_t *q;  // bf16 [R][64][512]
   const uint8_t *kv;  // bf16 latent rows of 512
@@ -135,7 +139,7 @@ struct MlaArgs {
   const int32_t *topk_lens; // [R]
   float scale;
   int32_t nsplit; // chunks per row
-  int32_t chunk;  // listed entries per chunk, a multiple of 16
+  int32_t chunk;  // listed entries per chunk, a multiple of 16, <= kMlaMaxChunk
   float *ws_o;    // [R][nsplit][64][512]
   float *ws_ml;   // [R][nsplit][64][2]
   uint16_t *out;  // bf16 [R][64][512]
