@@ -557,14 +557,16 @@ def q_quant_bench(args, torch, idx, R_decode):
 
 def sparse_mla_bench(args, torch, idx, synth):
     """Sparse attention over the decode batch's selection: 64 rows, 2048
-    listed tokens each (512-dim bf16 latent rows, page 64), 64 heads. Calls
+    listed tokens each in ascending token order, as the top-k writes them
+    (512-dim bf16 latent rows, page 64), 64 heads. Calls
     rotate over four copies of the latent cache (each call's 134 MB of rows
     was last touched three calls earlier, beyond the 256 MiB last-level
     cache), timed back to back between two events."""
     import numpy as np
     rng = np.random.default_rng(9)
     lens = rng.integers(2048, 32768 + 1, size=64)
-    case = synth.mla_case(lens, next_n=1, P=64, k=2048, seed=10)
+    # lists in ascending token order, as idx_topk writes them
+    case = synth.mla_case(lens, next_n=1, P=64, k=2048, seed=10, ascending=True)
     R, k = case.R, case.k
     q = torch.from_numpy(case.q.view(np.int16)).cuda()
     data = torch.from_numpy(case.data).cuda()

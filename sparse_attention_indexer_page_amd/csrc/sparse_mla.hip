@@ -9,25 +9,27 @@
 //
 // Split over tokens (flash decoding): work group (split, r) = 8 waves, wave w
 // owning heads 16 (w & 3) .. + 15 and output dims 256 (w >> 2) .. + 255,
-// scores a contiguous chunk of row r's list in blocks of 16 tokens:
+// scores a contiguous chunk of row r's list in blocks of 32 tokens:
 //   * a prologue resolves every listed token of the chunk through the block
 //     table once and keeps the byte offsets of their latent rows in LDS; the
-//     wave's 16 query heads stay in VGPRs as MFMA B operands;
-//   * the rows of a block (16 KB; thread t loads 32 bytes of row t / 32) are
-//     loaded into registers three blocks ahead of the one being scored, so
-//     each work group keeps 48 KB of reads in flight, then written into one
-//     of two LDS slots (rows padded to 1040 bytes so the four token rows one
-//     P.V operand read touches fall in distinct banks); a skipped entry
-//     reads a fixed in-bounds row and is stored as zeros. (Direct-to-LDS
-//     loads would save the register hop, but the compiler then waits for
-//     every one in flight before any LDS read of the ring.)
-//   * S^T = K q^T on v_mfma_f32_16x16x32_bf16 (tokens x heads, 512 dims = 16
-//     k-steps); both waves of a head group compute it, so each holds the
-//     scores of its heads without an exchange;
-//   * online softmax per head; the scores come out of that MFMA in exactly
-//     the A-operand layout of the P.V product (lane l: head l & 15, tokens
-//     4g..4g+3), so P needs no shuffle, only bf16 rounding;
-//   * O += P V on v_mfma_f32_16x16x16_bf16 (heads x 16 dims, K = the 16
+//     wave's 16 query heads (its 256 dims of them) stay in VGPRs as MFMA B
+//     operands;
+//   * the rows of a block (32 KB; thread t loads 64 bytes of row t / 16) are
+//     loaded into registers four blocks ahead of the one being scored (three
+//     blocks, 96 KB per work group, stay in flight at every wait), then
+//     written into one of two LDS slots (rows padded to 1040 bytes); a
+//     skipped entry reads a fixed in-bounds row and is stored as zeros.
+//     (Direct-to-LDS loads would save the register hop, but the compiler then
+//     waits for every one in flight before any LDS read of the slots.)
+//   * S^T = K q^T on v_mfma_f32_16x16x32_bf16 (tokens x heads, two 16-token
+//     tiles): the two waves of a head group each take 8 of the 16 k-steps
+//     (256 dims) and swap their partial tiles through LDS, both summing them
+//     in the same order, so both hold the same scores;
+//   * online softmax per head over the block; the scores come out of that
+//     MFMA in the A-operand layout of the P.V product (lane l: head l & 15,
+//     k-slots 8g..8g+7 = tokens 4g..4g+3 of both tiles), so P needs no
+//     shuffle, only bf16 rounding;
+//   * O += P V on v_mfma_f32_16x16x32_bf16 (heads x 16 dims, K = the 32
 //     tokens), 16 tiles for the wave's 256 dims, fp32 accumulators in VGPRs.
 // Each chunk leaves (max, sum, unnormalized O) per head in the workspace; a
 // second launch merges the chunks of every (row, head) and writes bf16 out
@@ -41,13 +43,12 @@ namespace {
 using namespace dev;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kMlaHeads = 64;
 constexpr int kMlaDim = 512;
-constexpr int kBlk = 16;                   // tokens per block
+constexpr int kBlk = 32;                   // tokens per block (two 16-token tiles)
 constexpr int kTileRow = 2 * kMlaDim + 16; // LDS bytes per staged row
-constexpr int kAhead = 3;                  // blocks loaded ahead of the one being scored
+constexpr int kAhead = 4;                  // blocks loaded ahead of the one being scored
 constexpr int kThreads = 512;              // 4 head groups x 2 dim halves
 constexpr int kWaveDims = kMlaDim / 2;     // output dims per wave
 
@@ -63,69 +64,109 @@ __device__ inline void lds_only_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row swaps: no LDS round trip, and every lane adds
+// the same operands in the same order.
+__device__ inline float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 struct MlaState {
-  v8bf qb[kMlaDim / 32]; // head col of the wave's group, dims 32 kk + 8 g .. + 8
+  v8bf qb[kWaveDims / 32]; // head col of the wave's group, dims 256 dh + 32 kk + 8 g .. + 8
   v4f O[kWaveDims / 16]; // heads 4g + jj, dims 16 dt + col of the wave's half
   float m_run, l_run;    // head col of the wave's group
 };
 
-// Scores one block from its LDS slot (all 16 rows resident); dh: the wave's
-// dim half.
+// Token of P.V k-slot 8 g + i: slots 0..3 of lane group g are tile 0's
+// tokens 4g..4g+3, slots 4..7 tile 1's (16 + 4g ..), which is where the
+// score MFMAs leave them, so P needs no shuffle.
+__device__ inline int pv_token(int g, int i) { return i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4); }
+
+// Scores one block from its LDS slot (all 32 rows resident); dh: the wave's
+// dim half; xch: the work group's exchange area for partial score tiles
+// (two v4f per lane and wave).
 __device__ inline void score_block(const MlaArgs &a, MlaState &S, const uint8_t *tile, int dh,
-                                   const int64_t *row_off_blk) {
+                                   v4f *xch, const int64_t *row_off_blk) {
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int col = lane & 15;
-  // ---- S^T = K q^T: lane holds head col, tokens 4g..4g+3 (A: token col,
-  // B: head col, both dims 32 kk + 8 g .. + 8)
-  v4f st = {0.f, 0.f, 0.f, 0.f};
+  // ---- partial S^T = K q^T of both 16-token tiles over the wave's 256
+  // dims: lane holds head col, tokens 16 tt + 4g..+3 (A: token col, B: head
+  // col, both dims 256 dh + 32 kk + 8 g .. + 8); two independent chains
+  v4f part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const uint8_t *kt = tile + col * kTileRow + 2 * kWaveDims * dh + 16 * g;
 #pragma unroll
-  for (int kk = 0; kk < kMlaDim / 32; ++kk) {
-    const v8bf ka = *reinterpret_cast<const v8bf *>(tile + col * kTileRow + 64 * kk + 16 * g);
-    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, S.qb[kk], st, 0, 0, 0);
-    if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0); // operands of four steps at a time
+  for (int kk = 0; kk < kWaveDims / 32; ++kk) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const v8bf ka = *reinterpret_cast<const v8bf *>(kt + 16 * tt * kTileRow + 64 * kk);
+      part[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, S.qb[kk], part[tt], 0, 0, 0);
+    }
+    if ((kk & 1) == 1) __builtin_amdgcn_sched_barrier(0); // operands of four MFMAs at a time
   }
-  // ---- online softmax over the block, per head
-  float s[4];
+  // ---- the partner wave (other dim half, same heads) holds the other
+  // half of the sums; both add dim half 0 + dim half 1
+  xch[wave * 64 + lane] = part[0];
+  xch[kThreads + wave * 64 + lane] = part[1];
+  lds_only_barrier();
+  float s[2][4];
   float bm = -__builtin_huge_valf();
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    s[jj] = row_off_blk[4 * g + jj] >= 0 ? st[jj] * a.scale : -__builtin_huge_valf();
-    bm = fmaxf(bm, s[jj]);
+  for (int tt = 0; tt < 2; ++tt) {
+    const v4f other = xch[tt * kThreads + (wave ^ 4) * 64 + lane];
+    const v4f st = dh == 0 ? part[tt] + other : other + part[tt];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      s[tt][jj] = row_off_blk[16 * tt + 4 * g + jj] >= 0 ? st[jj] * a.scale : -__builtin_huge_valf();
+      bm = fmaxf(bm, s[tt][jj]);
+    }
   }
-  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  // ---- online softmax over the block, per head
+  bm = rows_max(bm);
   const float m_new = fmaxf(S.m_run, bm);
   const float alpha = S.m_run == -__builtin_huge_valf() ? 0.f : __expf(S.m_run - m_new);
-  float p[4], ls = 0.f;
+  float p[2][4], ls = 0.f;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    p[jj] = s[jj] == -__builtin_huge_valf() ? 0.f : __expf(s[jj] - m_new);
-    ls += p[jj];
-  }
-  ls += __shfl_xor(ls, 16, 64);
-  ls += __shfl_xor(ls, 32, 64);
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      p[tt][jj] = s[tt][jj] == -__builtin_huge_valf() ? 0.f : __expf(s[tt][jj] - m_new);
+      ls += p[tt][jj];
+    }
+  ls = rows_sum(ls);
   S.l_run = S.l_run * alpha + ls;
   S.m_run = m_new;
   // O rows are heads 4g + jj: their factors live in lanes 4g + jj
   float ah[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) ah[jj] = __shfl(alpha, 4 * g + jj, 64);
-  // P as the A operand: head col, tokens 4g..4g+3, bf16
-  const v4s pa = v4s{(short)bf16_rne(p[0]), (short)bf16_rne(p[1]), (short)bf16_rne(p[2]),
-                     (short)bf16_rne(p[3])};
+  // P as the A operand of the 16x16x32 product: head col, k-slots 8g..8g+7
+  v8bf pa;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    pa[i] = __builtin_bit_cast(__bf16, (uint16_t)bf16_rne(p[i >> 2][i & 3]));
   const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile) + kWaveDims * dh;
 #pragma unroll
   for (int dt = 0; dt < kWaveDims / 16; ++dt) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) S.O[dt][jj] *= ah[jj];
-    v4s vb;
+    v8bf vb;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      vb[jj] = (short)t16[((4 * g + jj) * kTileRow) / 2 + 16 * dt + col];
-    S.O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, S.O[dt], 0, 0, 0);
-    // keep the V reads of at most four tiles in flight
-    if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 8; ++i)
+      vb[i] = __builtin_bit_cast(__bf16, t16[(pv_token(g, i) * kTileRow) / 2 + 16 * dt + col]);
+    S.O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, S.O[dt], 0, 0, 0);
+    // keep the V reads of at most two tiles in flight
+    if ((dt & 1) == 1) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -133,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_partial_kernel(MlaArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kBlk * kTileRow];
   // byte offset of each listed row (-1: skipped, or past the chunk, up to
   // the last block loaded ahead)
-  __shared__ int64_t row_off[kMlaMaxChunk + (2 * kAhead - 1) * kBlk];
+  __shared__ int64_t row_off[kMlaMaxChunk + 2 * kAhead * kBlk];
   const int sp = blockIdx.x;
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
@@ -143,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_partial_kernel(MlaArgs a)
   const int dh = wave >> 2; // dim half
   const int g = lane >> 4;
   const int col = lane & 15;
+  __shared__ v4f xch[2 * kThreads]; // partial score tiles, two per lane
   const int b = r / a.next_n;
   int n = uniform_load(a.topk_lens + r);
   n = n < 0 ? 0 : (n > a.k ? a.k : n);
@@ -171,9 +213,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_partial_kernel(MlaArgs a)
     row_off[i] = off;
   }
   MlaState S;
-  const uint16_t *qh = a.q + ((int64_t)r * kMlaHeads + 16 * hg + col) * kMlaDim;
+  const uint16_t *qh = a.q + ((int64_t)r * kMlaHeads + 16 * hg + col) * kMlaDim + kWaveDims * dh;
 #pragma unroll
-  for (int kk = 0; kk < kMlaDim / 32; ++kk)
+  for (int kk = 0; kk < kWaveDims / 32; ++kk)
     S.qb[kk] = *reinterpret_cast<const v8bf *>(qh + 32 * kk + 8 * g);
 #pragma unroll
   for (int dt = 0; dt < kWaveDims / 16; ++dt) S.O[dt] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -182,44 +224,44 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_partial_kernel(MlaArgs a)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); // the queries, before any block load is counted
   __syncthreads();                           // the table is complete
 
-  // thread t carries bytes [16 (t & 31), + 16) and [512 + 16 (t & 31), + 16)
-  // of row t >> 5 of a block (each load instruction reads two half rows)
-  const int gj = tid >> 5;
-  const int gs = tid & 31;
+  // thread t carries bytes [256 u + 16 (t & 15), + 16), u = 0..3, of row
+  // t >> 4 of a block (each load instruction reads 256 contiguous bytes of
+  // four rows)
+  const int gj = tid >> 4;
+  const int gs = tid & 15;
   // Loads of block bi; rows past the chunk (and skipped entries) read the
   // cache's first row, inside every valid cache, and are zeroed when stored,
   // so every path keeps the same loads in flight.
-  auto load_block = [&](int bi, v4i (&v)[2]) {
+  auto load_block = [&](int bi, v4i (&v)[4]) {
     const int64_t off = row_off[bi * kBlk + gj];
     const v4i *src = reinterpret_cast<const v4i *>(a.kv + (off >= 0 ? off : 0) + 16 * gs);
-    v[0] = src[0];
-    v[1] = src[32];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[16 * u];
   };
-  auto store_block = [&](int bi, const v4i (&v)[2]) {
+  auto store_block = [&](int bi, const v4i (&v)[4]) {
     const bool ok = row_off[bi * kBlk + gj] >= 0;
     v4i *dst = reinterpret_cast<v4i *>(tile[bi & 1] + gj * kTileRow + 16 * gs);
-    dst[0] = ok ? v[0] : v4i{0, 0, 0, 0};
-    dst[32] = ok ? v[1] : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[16 * u] = ok ? v[u] : v4i{0, 0, 0, 0};
   };
   // One block: store it (its slot was last read two blocks ago, before the
-  // previous barrier), publish it, refill its registers three blocks ahead
-  // and score it.
-  auto step = [&](int bi, v4i (&v)[2]) {
+  // previous barrier), publish it, refill its registers kAhead blocks ahead
+  // and score it. The exchange area is rewritten only after the next
+  // block's first barrier, which every wave reaches after reading it.
+  auto step = [&](int bi, v4i (&v)[4]) {
     store_block(bi, v);
     lds_only_barrier();
     load_block(bi + kAhead, v);
-    score_block(a, S, tile[bi & 1], dh, row_off + bi * kBlk);
+    score_block(a, S, tile[bi & 1], dh, xch, row_off + bi * kBlk);
   };
 
-  v4i ra[2], rb[2], rc[2];
+  v4i rg[kAhead][4]; // register ring: block bi lives in rg[bi % kAhead]
   if (nblk > 0) {
-    load_block(0, ra);
-    load_block(1, rb);
-    load_block(2, rc);
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) load_block(u, rg[u]);
     for (int bi = 0; bi < nblk; bi += kAhead) {
-      step(bi, ra);
-      step(bi + 1, rb);
-      step(bi + 2, rc);
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) step(bi + u, rg[u]);
     }
   }
 

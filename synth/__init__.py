@@ -452,9 +452,10 @@ class MlaCase:
 
 
 def mla_case(lens, *, next_n=1, P=64, k=2048, H=64, D=512, row_stride=None, seed=0,
-             full=False, holes=False):
+             full=False, holes=False, ascending=False):
     """Selected lists: each row picks min(k, E_r) distinct tokens of its
-    visible window (E_r as in decode) in random order, or every visible token
+    visible window (E_r as in decode) in random order (ascending: in
+    increasing token order, as the top-k writes them), or every visible token
     when full; holes sets a few entries inside the count to -1."""
     rng = rng_for(seed)
     lens = np.asarray(lens, dtype=np.int64)
@@ -489,6 +490,8 @@ def mla_case(lens, *, next_n=1, P=64, k=2048, H=64, D=512, row_stride=None, seed
         E = max(0, int(lens[b]) - (next_n - 1 - j))
         n = min(k, E)
         sel = np.arange(E) if full else rng.permutation(E)[:n]
+        if ascending:
+            sel = np.sort(sel)
         if not full:
             idx[r, :n] = sel
         else:
