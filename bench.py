@@ -429,14 +429,18 @@ def summarize_mfma(pmc_dir):
                      "mfma_busy_cycles": c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0),
                      "grbm_gui_active": c.get("GRBM_GUI_ACTIVE", 0.0),
                      "us": dur[did] * 1e6, "tflops": flops / dur[did] / 1e12})
-    big = [r for r in rows if r["mfma_insts"] >= 0.5 * max(x["mfma_insts"] for x in rows)]
-    avg = lambda key: sum(r[key] for r in big) / len(big)
-    # MFMA busy cycles are summed over the 1024 SIMDs (one 16x16x128 FP8 MFMA
-    # keeps a SIMD busy 32 cycles); against the traced duration at the
-    # 2.4 GHz peak engine clock this is a lower bound on the busy fraction.
-    busy_frac = avg("mfma_busy_cycles") / (1024 * avg("us") * 1e-6 * 2.4e9)
+    big = rows  # every chunk's dispatch of every call
+    tot = lambda key: sum(r[key] for r in big)
+    # Aggregates over all dispatches: flops and busy cycles over the summed
+    # traced durations. MFMA busy cycles are summed over the 1024 SIMDs (one
+    # 16x16x128 FP8 MFMA keeps a SIMD busy 32 cycles); against the traced
+    # duration at the 2.4 GHz peak engine clock this is a lower bound on the
+    # busy fraction.
+    agg_tflops = tot("mfma_insts") * FP8_MFMA_FLOPS / (tot("us") * 1e-6) / 1e12
+    busy_frac = tot("mfma_busy_cycles") / (1024 * tot("us") * 1e-6 * 2.4e9)
+    avg = lambda key: tot(key) / len(big)
     summary = {
-        "kernel": "prefill_logits_kernel<FP8, 4 tiles> (first chunk: 15625 rows)",
+        "kernel": "prefill_logits_kernel<FP8, 4 tiles> (both chunks: 8192 + 8192 rows)",
         "workload": "chunked prefill: 16384 rows over 4096 keys, causal (r+1)//4, page 64",
         "kernel_source_digest": prefill_source_digest(),
         "commands": [
@@ -448,8 +452,8 @@ def summarize_mfma(pmc_dir):
         "dispatches": big,
         "mfma_insts_per_dispatch": avg("mfma_insts"),
         "us_per_dispatch": avg("us"),
-        "fp8_tflops": avg("tflops"),
-        "fp8_mfma_frac": avg("tflops") / FP8_MFMA_PEAK_TFLOPS,
+        "fp8_tflops": agg_tflops,
+        "fp8_mfma_frac": agg_tflops / FP8_MFMA_PEAK_TFLOPS,
         "mfma_busy_frac_at_2p4ghz": busy_frac,
     }
     with open(MFMA_SUMMARY + ".json", "w") as fh:
@@ -459,15 +463,16 @@ def summarize_mfma(pmc_dir):
         fh.write("Commands (repository root, one MI355X):\n\n```\n%s\n```\n\n" %
                  "\n".join(summary["commands"]))
         fh.write("`bench.py --prefill-counters` runs the 16384-row prefill call three times "
-                 "(budget 256e6 B: a 15625-row chunk and a 759-row chunk). Rows below are the "
-                 "first-chunk dispatches.\n\n")
+                 "(budget 256e6 B: two chunks of 8192 rows; the first sees 0-2048 keys per row, "
+                 "the second 2048-4096). Rows below are every chunk's dispatch.\n\n")
         fh.write("| dispatch | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | "
                  "traced us | FP8 TFLOP/s |\n|---|---|---|---|---|---|\n")
         for r in big:
             fh.write("| %d | %s | %s | %s | %.1f | %.0f |\n" % (
                 r["dispatch"], f"{r['mfma_insts']:,.0f}", f"{r['mfma_busy_cycles']:,.0f}",
                 f"{r['grbm_gui_active']:,.0f}", r["us"], r["tflops"]))
-        fh.write("\nFP8 flops = SQ_INSTS_MFMA x %d (one 16x16x128 FP8 MFMA); average %.0f "
+        fh.write("\nFP8 flops = SQ_INSTS_MFMA x %d (one 16x16x128 FP8 MFMA); summed over all "
+                 "dispatches and divided by their summed traced durations: %.0f "
                  "TFLOP/s = %.1f%% of the 5.0 PFLOP/s dense FP8 peak. SQ_VALU_MFMA_BUSY_CYCLES "
                  "over 1024 SIMDs x traced duration x 2.4 GHz: %.1f%% busy (a lower bound if the "
                  "engine clock ran below 2.4 GHz). GRBM_GUI_ACTIVE is listed as read. Kernel "

@@ -233,8 +233,9 @@ idx_status idx_topk(const float *logits, int64_t W, const int32_t *context_lens,
  * max(1, floor(budget_bytes / (4*W))) (host only). */
 int64_t idx_prefill_rows_per_chunk(int64_t W, int64_t budget_bytes);
 
-/* Logits scratch bytes idx_prefill_chunked_topk needs: 4*W*min(T, rows per
- * chunk) (host only). */
+/* Logits scratch bytes idx_prefill_chunked_topk needs: 4*W*ceil(T/n), where
+ * n = ceil(T / rows per chunk) is the number of chunks the budget requires
+ * and the rows are spread evenly over them (host only). */
 int64_t idx_prefill_scratch_bytes(int32_t T, int64_t W, int64_t budget_bytes);
 
 /* int32 entries of cta_scratch idx_prefill_chunked_topk needs. */

@@ -106,13 +106,18 @@ int64_t prefill_rows_per_chunk(int64_t W, int64_t budget) {
 }
 
 // Rows of one prefill chunk actually used: the budget rule, capped so the
-// schedule builder's segment scan fits in LDS (the result does not depend on
-// the chunking).
+// schedule builder's segment scan fits in LDS, then spread evenly over the
+// chunks that rule needs (n = ceil(T / max rows), ceil(T / n) rows each), so
+// no chunk is a small remainder that leaves most of the chip idle (the
+// result does not depend on the chunking).
 int64_t prefill_chunk_rows(int32_t T, int64_t W, int64_t budget) {
   int64_t rows = prefill_rows_per_chunk(W, budget);
   const int64_t cap = (int64_t)idx::kMaxSegs * idx::kPrefillRowsPerSeg;
   if (rows > cap) rows = cap;
   if (rows > T) rows = T;
+  if (rows < 1) rows = 1;
+  const int64_t n = (T + rows - 1) / rows;
+  rows = (T + n - 1) / n; // <= the budget's rows
   return rows < 1 ? 1 : rows;
 }
 

@@ -164,10 +164,13 @@ def test_prefill_chunk_rule_reproduces_the_pages_buffer_sizes():
     assert right == 4 * T * g["right_sized_width"]
     assert round(right / 1e6) == g["right_sized_bytes_approx_mb"]
     # The decimal 256 MB budget of the chunked-prefill workload forces two
-    # chunks: 15625 rows, then 759.
+    # chunks (at most 15625 rows each); the rows are spread evenly over them,
+    # 8192 + 8192, so the scratch holds 8192 rows.
     rows = idx.idx_prefill_rows_per_chunk(4096, 256_000_000)
     assert rows == 15625 and -(-T // rows) == 2
-    assert idx.idx_prefill_scratch_bytes(T, 4096, 256_000_000) == 4 * 4096 * 15625
+    assert idx.idx_prefill_scratch_bytes(T, 4096, 256_000_000) == 4 * 4096 * 8192
+    # Uneven counts: 3 chunks of at most 5 rows for 11 rows -> 4 rows each.
+    assert idx.idx_prefill_scratch_bytes(11, 4096, 4 * 4096 * 5) == 4 * 4096 * 4
     # One row per chunk at a budget below one row.
     assert idx.idx_prefill_rows_per_chunk(4096, 1) == 1
 

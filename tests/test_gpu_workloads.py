@@ -130,8 +130,11 @@ def test_workload4_chunked_prefill():
     case = synth.workload(4)
     dc = DeviceCase(case)
     assert idx.idx_prefill_rows_per_chunk(case.W, case.budget_bytes) == 15625
-    scratch, out = run_prefill(dc)  # two chunks: [0, 15625), [15625, 16384)
     T, W, k = case.T, case.W, case.k
+    # two chunks (at most 15625 rows each), spread evenly: [0, 8192), [8192, 16384)
+    c1 = idx.idx_prefill_scratch_bytes(T, W, case.budget_bytes) // (4 * W)
+    assert c1 == 8192
+    scratch, out = run_prefill(dc)
     E_all = case.visible_end.astype(np.int64)
     o = out.numpy()
     for r in range(T):  # whole output: short rows select everything
@@ -142,15 +145,15 @@ def test_workload4_chunked_prefill():
             assert np.array_equal(o[r, :n], np.arange(n))
         else:
             assert np.all(np.diff(o[r, :n]) > 0) and o[r, 0] >= 0 and o[r, n - 1] < e
-    rows = [0, 2, 3, 4, 8191, 8195, 12000, 15624, 15625, 15626, 16000, 16383]
+    rows = [0, 2, 3, 4, 8191, 8192, 8195, 12000, 15624, 15625, 15626, 16000, 16383]
     ref, E = oracle_prefill_rows(case, rows)
     for i, r in enumerate(rows):
         check_topk_band(o[r], ref[i], E[i], k, "w4 row %d" % r)
     # logits of the second chunk are still in the scratch buffer
-    lg = scratch.numpy()[: (T - 15625) * W].reshape(T - 15625, W)
+    lg = scratch.numpy()[: (T - c1) * W].reshape(T - c1, W)
     for i, r in enumerate(rows):
-        if r >= 15625:
-            check_logits(lg[r - 15625], ref[i], E[i], "w4 logits row %d" % r)
+        if r >= c1:
+            check_logits(lg[r - c1], ref[i], E[i], "w4 logits row %d" % r)
     # one chunk (the whole [T, W] buffer) gives identical indices
     scratch1, out1 = run_prefill(dc, budget=4 * W * T)
     assert torch.equal(out1, out)
