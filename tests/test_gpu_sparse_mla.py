@@ -72,6 +72,20 @@ def test_sparse_mla_matches_oracle(P, next_n, row_stride, scale):
     _check(case, scale, got, lse)
 
 
+def test_sparse_mla_one_chunk_per_row_and_odd_list_length():
+    """300 rows (next_n 2) with lists of at most 100 entries: one chunk per
+    row (no split), a list length that is not a multiple of the 32-token
+    block, plus skipped entries."""
+    log("sparse mla one chunk per row")
+    rng = np.random.default_rng(73)
+    lens = rng.integers(0, 400, size=150)
+    lens[:3] = [0, 1, 101]
+    case = synth.mla_case(lens, next_n=2, P=64, k=100, seed=74, holes=True)
+    assert idx.idx_sparse_mla_workspace_size(case.R, case.k) == case.R * 64 * (512 + 2) * 4
+    got, lse = _run(case, 0.8)
+    _check(case, 0.8, got, lse)
+
+
 def test_sparse_mla_full_size_sampled_rows():
     """64 rows, 2048 selected tokens each (the decode batch's top-k), page 64."""
     log("sparse mla full size")
