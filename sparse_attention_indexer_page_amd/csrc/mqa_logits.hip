@@ -253,6 +253,21 @@ template <int TPB> struct KBlock {
   int t0;           // first token of the block
 };
 
+// Key bytes and key scales are read once per launch: the loads carry the
+// non-temporal hint (cache policy nt), so the stream does not displace the
+// small data every launch reuses (lengths, block tables, queries, weights)
+// or the logits the top-k reads next (decode scoring 35.6 -> 33.4 us on the
+// batched-decode workload, measured).
+constexpr int kStream = 2; // buffer-load aux bits: nt
+
+__device__ inline v4i load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
+}
+
+__device__ inline uint32_t load4_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStream);
+}
+
 // Physical page of logical page lp of sequence s, or -1 past the table row.
 // A scalar load: waiting for it never waits for the K loads in flight.
 __device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp) {
@@ -291,18 +306,18 @@ __device__ inline void issue_block_page(const LogitsArgs &a, int blk, int64_t pg
     // one scale per lane: the token this lane holds after the head-sum
     // reduction (t0 + lane for 4-tile blocks, t0 + 16*(g/2) + col for 2-tile)
     const uint32_t slot = (uint32_t)(slot0 + (TPB == 4 ? lane : 16 * (g >> 1) + col));
-    kb.ksr = load4(sr, slot * (uint32_t)a.scale_row_stride);
+    kb.ksr = load4_stream(sr, slot * (uint32_t)a.scale_row_stride);
   }
 #pragma unroll
   for (int ti = 0; ti < TPB; ++ti) {
     const uint32_t slot = (uint32_t)(slot0 + ti * kTile + col);
     const uint32_t off = slot * (uint32_t)a.row_stride;
     if (DT == IDX_FP8_E4M3) {
-      kb.kb[ti] = cat(load16(kr, off + 16 * g), load16(kr, off + 64 + 16 * g));
+      kb.kb[ti] = cat(load16_stream(kr, off + 16 * g), load16_stream(kr, off + 64 + 16 * g));
     } else {
-      const v4i lo = load16(kr, off + 16 * g);
+      const v4i lo = load16_stream(kr, off + 16 * g);
       kb.kb[ti] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-      kb.ks[ti] = load4(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
+      kb.ks[ti] = load4_stream(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
     }
   }
 }
