@@ -399,7 +399,9 @@ const char *idx_last_error(void);
 
 /* ABI version of this library (major*10000 + minor*100 + patch). 0.2.0 adds
  * the K-cache writer, the query quantizer, ragged decode, the prefill
- * index_base argument, query flags and decode without a schedule buffer. */
+ * index_base argument, query flags and decode without a schedule buffer;
+ * 0.3.0 adds the sparse attention over the selection and spreads prefill rows
+ * evenly over the chunks the budget requires. */
 int32_t idx_version(void);
 
 #ifdef __cplusplus

@@ -134,7 +134,7 @@ int32_t prefill_ctas(int64_t chunk_rows) {
 
 extern "C" {
 
-int32_t idx_version(void) { return 200; }
+int32_t idx_version(void) { return 300; }
 
 const char *idx_status_string(idx_status s) {
   switch (s) {
