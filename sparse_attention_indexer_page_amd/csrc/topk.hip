@@ -42,21 +42,52 @@ __device__ inline float key_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-template <typename T> __device__ inline T wave_reduce_max(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const T o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+// Sum over the wave's 64 lanes, in every lane, without LDS: quad swaps, the
+// half-row and row mirrors (DPP), then the gfx950 row swaps.
+__device__ inline uint32_t wave_sum(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false); // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false); // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] + a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] + b[1];
 }
 
-template <typename T> __device__ inline T wave_reduce_min(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const T o = __shfl_xor(v, off, 64);
-    v = o < v ? o : v;
-  }
+// Max / min over the wave's 64 lanes, in every lane, the same way.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(b[0], b[1]);
+}
+
+// Inclusive prefix sum over the wave's lanes with DPP moves: shifts by 1, 2,
+// 4, 8 within each 16-lane row (lanes shifted in from outside the row add
+// 0), then row 0's total into rows 1 and 3 and row 1's into rows 2 and 3
+// (row_bcast 15), then the first half's into the second (row_bcast 31).
+__device__ inline uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false); // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false); // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false); // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false); // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false); // row_bcast:31
   return v;
 }
 
@@ -126,12 +157,7 @@ __device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit
     cnt[q] = sm.hist[top - q];
     mine += cnt[q];
   }
-  uint32_t incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan_u32(mine);
   if (lane == 63) sm.red[wave] = incl;
   __syncthreads();
   uint32_t before = 0;
@@ -162,8 +188,8 @@ __device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  mx = wave_reduce_max(mx);
-  mn = wave_reduce_min(mn);
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
   __syncthreads(); // red is free
   if (lane == 0) {
     sm.red[wave] = mx;
@@ -269,16 +295,21 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   if (!done && !in_lds && cand > kRankCap && cand <= kCandCap) {
     in_lds = true;
     nc = cand;
+    // the wave's candidates are counted from ballots first, so the wave
+    // reserves its slots with one LDS atomic instead of one per item
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) mine += key[i] >= lo && key[i] <= hi ? 1u : 0u;
+    const uint32_t tot = wave_sum(mine);
+    uint32_t at = 0;
+    if (lane == 0 && tot != 0u) at = atomicAdd(&sm.ncand, tot);
+    at = __builtin_amdgcn_readlane(at, 0);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const bool c = key[i] >= lo && key[i] <= hi;
       const uint64_t m = __ballot(c);
-      if (m) {
-        uint32_t at = 0;
-        if (lane == 0) at = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
-        at = __shfl(at, 0, 64);
-        if (c) sm.cand[at + lanes_below(m)] = key[i];
-      }
+      if (c) sm.cand[at + lanes_below(m)] = key[i];
+      at += (uint32_t)__popcll(m);
     }
     __syncthreads();
   }
@@ -296,7 +327,7 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
         if (m) {
           uint32_t at = 0;
           if (lane == 0) at = atomicAdd(&sm.nsmall, (uint32_t)__popcll(m));
-          at = __shfl(at, 0, 64);
+          at = __builtin_amdgcn_readlane(at, 0);
           if (c) sm.small[at + lanes_below(m)] = x;
         }
       };
@@ -311,8 +342,21 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
         }
         __syncthreads();
       } else {
+        // from the registers: count, one reservation per wave, then write
+        uint32_t mine = 0;
 #pragma unroll
-        for (int i = 0; i < IPT; ++i) put(key[i], key[i] >= lo && key[i] <= hi);
+        for (int i = 0; i < IPT; ++i) mine += key[i] >= lo && key[i] <= hi ? 1u : 0u;
+        const uint32_t tot = wave_sum(mine);
+        uint32_t at = 0;
+        if (lane == 0 && tot != 0u) at = atomicAdd(&sm.nsmall, tot);
+        at = __builtin_amdgcn_readlane(at, 0);
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+          const bool c = key[i] >= lo && key[i] <= hi;
+          const uint64_t m = __ballot(c);
+          if (c) sm.small[at + lanes_below(m)] = key[i];
+          at += (uint32_t)__popcll(m);
+        }
         __syncthreads();
       }
       if (wave == 0) {
@@ -523,12 +567,7 @@ __device__ __forceinline__ void wave_radix_pass(WaveShared &sm, const uint32_t (
   uint32_t mine = 0;
 #pragma unroll
   for (int q = 0; q < 16; ++q) mine += cnt[q];
-  uint32_t incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan_u32(mine);
   const uint32_t excl = incl - mine;
   const bool holder = excl < (uint32_t)need && incl >= (uint32_t)need;
   uint32_t my_bin = 0, my_above = 0, my_in = 0;
@@ -572,8 +611,8 @@ __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, 
       kmin = key[i] < kmin ? key[i] : kmin;
     }
   }
-  kmax = wave_reduce_max(kmax);
-  kmin = wave_reduce_min(kmin);
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
 
   // The candidates are the keys in [lo, hi]; `need` of them remain to take.
   uint32_t lo = kmin, hi = kmax;
