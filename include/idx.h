@@ -238,7 +238,9 @@ int64_t idx_prefill_rows_per_chunk(int64_t W, int64_t budget_bytes);
  * and the rows are spread evenly over them (host only). */
 int64_t idx_prefill_scratch_bytes(int32_t T, int64_t W, int64_t budget_bytes);
 
-/* int32 entries of cta_scratch idx_prefill_chunked_topk needs. */
+/* int32 entries of cta_scratch idx_prefill_chunked_topk needs: one schedule
+ * (idx_schedule_ints of the chunk's work-group count) per chunk, all built by
+ * one launch before the first chunk is scored. */
 int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes);
 
 /*
@@ -264,8 +266,9 @@ int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes);
  *                  that page's FP8 prefill path. index_base + W < 2^31.
  *   out_idx        int32 [T][k], ascending indices as in idx_topk, plus
  *                  index_base
- * The host loop over chunks enqueues schedule, scores and top-k per chunk on
- * `stream` without synchronizing.
+ * One launch builds every chunk's schedule (each encodes its chunk's absolute
+ * rows, in its own part of cta_scratch); the host loop over chunks then
+ * enqueues scores and top-k per chunk on `stream` without synchronizing.
  * Errors: as idx_paged_mqa_logits and idx_topk; IDX_ERR_WORKSPACE when a
  * scratch buffer is too small.
  */

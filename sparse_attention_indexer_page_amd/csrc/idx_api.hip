@@ -182,6 +182,9 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
   a.entry_cost = idx::kDecodeEntryCost;
   a.n_ctas = n_ctas;
   a.cta_info = cta_info;
+  a.n_chunks = 1;
+  a.chunk_rows = 0;
+  a.chunk_ints = 0;
   hipError_t e = idx::launch_schedule(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "schedule launch");
   return ok();
@@ -480,7 +483,9 @@ int64_t idx_prefill_scratch_bytes(int32_t T, int64_t W, int64_t budget_bytes) {
 
 int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes) {
   if (T < 1 || W < 1) return 0;
-  return idx_schedule_ints(prefill_ctas(prefill_chunk_rows(T, W, budget_bytes)));
+  const int64_t rows = prefill_chunk_rows(T, W, budget_bytes);
+  const int64_t chunks = (T + rows - 1) / rows;
+  return chunks * idx_schedule_ints(prefill_ctas(rows)); // one schedule per chunk
 }
 
 idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
@@ -509,17 +514,36 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
     return fail(IDX_ERR_WORKSPACE, "logits scratch %lld B < %lld B", (long long)scratch_bytes,
                 (long long)(4 * W * rows));
   const int32_t n_ctas = prefill_ctas(rows);
-  if (cta_scratch_ints < idx_schedule_ints(n_ctas))
+  const int64_t n_chunks = (T + rows - 1) / rows;
+  const int64_t sched_ints = idx_schedule_ints(n_ctas); // per chunk
+  if (cta_scratch_ints < n_chunks * sched_ints)
     return fail(IDX_ERR_WORKSPACE, "schedule scratch %lld ints < %lld", (long long)cta_scratch_ints,
-                (long long)idx_schedule_ints(n_ctas));
+                (long long)(n_chunks * sched_ints));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // every chunk's schedule in one launch (work group g builds chunk g's),
+  // before the first chunk is scored
+  idx::ScheduleArgs sa;
+  sa.lens = visible_end;
+  sa.nseg = (int32_t)((rows + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg);
+  sa.mode = idx::kSegPrefill;
+  sa.row0 = 0;
+  sa.row_end = T;
+  sa.block_tokens = idx::block_tokens(kv->page_size);
+  sa.entry_cost = idx::kPrefillEntryCost;
+  sa.n_ctas = n_ctas;
+  sa.cta_info = cta_scratch;
+  sa.n_chunks = (int32_t)n_chunks;
+  sa.chunk_rows = (int32_t)rows;
+  sa.chunk_ints = sched_ints;
+  if (n_chunks == 1) sa.row_end = (int32_t)rows;
+  hipError_t e = idx::launch_schedule(sa, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill schedule launch");
   idx::LogitsArgs la = logits_args(q, kv);
   la.block_tables = block_table;
   la.bt_stride = 0;
   la.bt_cols = (W + kv->page_size - 1) / kv->page_size;
   la.lens = visible_end;
   la.next_n = 1;
-  la.cta_info = cta_scratch;
   la.n_ctas = n_ctas;
   la.logits = logits_scratch;
   la.W = W;
@@ -527,18 +551,7 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
     const int64_t r1 = r0 + rows < T ? r0 + rows : T;
     const int32_t nseg =
         (int32_t)((r1 - r0 + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg);
-    idx::ScheduleArgs sa;
-    sa.lens = visible_end;
-    sa.nseg = nseg;
-    sa.mode = idx::kSegPrefill;
-    sa.row0 = (int32_t)r0;
-    sa.row_end = (int32_t)r1;
-    sa.block_tokens = la.block_tokens;
-    sa.entry_cost = idx::kPrefillEntryCost;
-    sa.n_ctas = n_ctas;
-    sa.cta_info = cta_scratch;
-    hipError_t e = idx::launch_schedule(sa, s);
-    if (e != hipSuccess) return hip_fail(e, "prefill schedule launch");
+    la.cta_info = cta_scratch + (r0 / rows) * sched_ints;
     la.nseg = nseg;
     la.row0 = (int32_t)r0;
     la.row_end = (int32_t)r1;

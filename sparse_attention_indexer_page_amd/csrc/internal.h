@@ -41,6 +41,12 @@ struct ScheduleArgs {
   int32_t entry_cost; // cost of entering a non-empty segment, in blocks
   int32_t n_ctas;
   int32_t *cta_info; // [n_ctas + 1][2]
+  // prefill: work group g builds the schedule of rows [row0 + g*chunk_rows,
+  // min(row0 + (g+1)*chunk_rows, row_end)) into cta_info + g*chunk_ints
+  // (n_chunks work groups; decode: 1)
+  int32_t n_chunks;
+  int32_t chunk_rows;
+  int64_t chunk_ints;
 };
 
 struct LogitsArgs {

@@ -46,6 +46,14 @@ __device__ inline int32_t segment_length(const ScheduleArgs &a, int s) {
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
+  if (a.mode == kSegPrefill && a.n_chunks > 1) { // this work group's chunk
+    const int g = blockIdx.x;
+    a.row0 += g * a.chunk_rows;
+    const int32_t end = a.row0 + a.chunk_rows;
+    a.row_end = end < a.row_end ? end : a.row_end;
+    a.nseg = (a.row_end - a.row0 + kPrefillRowsPerSeg - 1) / kPrefillRowsPerSeg;
+    a.cta_info += g * a.chunk_ints;
+  }
   // prefix[s] = cost of segments [0, s)
   extern __shared__ int32_t prefix[];
   __shared__ int32_t wave_tot[kWaves];
@@ -205,7 +213,7 @@ hipError_t launch_fill_tail(const int32_t *lens, const int32_t *row_offsets, int
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
   const size_t lds = sizeof(int32_t) * (size_t)(a.nseg > 0 ? a.nseg : 1);
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(schedule_kernel, dim3(a.n_chunks > 1 ? a.n_chunks : 1), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
