@@ -327,7 +327,7 @@ def prefill_bench(args, torch, idx, synth):
     for _ in range(2):
         call()
     torch.cuda.synchronize()
-    n = max(3, args.steps // 4)
+    n = max(20, args.steps // 4)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(n):
@@ -654,8 +654,8 @@ def cpu_baseline(case, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--ctas", type=int, default=0, help="schedule work groups (0: recommended)")
     ap.add_argument("--pool-copies", type=int, default=4)
     ap.add_argument("--split", choices=("auto", "buffer", "in-kernel"), default="auto",
