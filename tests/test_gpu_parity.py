@@ -227,13 +227,17 @@ def test_topk_all_equal_and_two_values():
     assert np.array_equal(o[2], np.arange(k))
 
 
+@pytest.mark.parametrize("P", [32, 64, 256])
 @pytest.mark.parametrize("dtype", [synth.FP8, synth.MXFP4])
-def test_prefill_small_matches_oracle_and_is_chunk_invariant(dtype):
-    log("prefill small dtype %d" % dtype)
+def test_prefill_small_matches_oracle_and_is_chunk_invariant(dtype, P):
+    """Every row against the oracle, then budgets of 4, 43 and 301 uneven
+    chunks (each chunk's schedule built by the one schedule launch) give the
+    same selection; pages of 32 rows use the two-tile key blocks."""
+    log("prefill small dtype %d P %d" % (dtype, P))
     T = 301
-    ve = np.minimum(2 * (np.arange(T) + 1), 600)  # ragged, several 64-token blocks
-    case = synth.prefill_case(T, 600, visible_end=ve, P=64, k=32, W=600, dtype=dtype,
-                              seed=900 + dtype)
+    ve = np.minimum(2 * (np.arange(T) + 1), 600)  # ragged, several key blocks
+    case = synth.prefill_case(T, 600, visible_end=ve, P=P, k=32, W=600, dtype=dtype,
+                              seed=900 + dtype + P)
     dc = DeviceCase(case)
     full_budget = 4 * case.W * case.T
     scratch, out = run_prefill(dc, budget=full_budget)
