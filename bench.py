@@ -83,7 +83,7 @@ def decode_bench(args, torch, idx, synth, wl=2, split=None):
     kvs = [idx.make_kv_cache(case.dtype, c.page_size, c.num_pages, pools[i], c.page_stride,
                              c.row_stride, scales[i], c.scale_page_stride, c.scale_row_stride)
            for i in range(n_sets)]
-    n_ctas = args.ctas or idx.idx_recommended_ctas(R)
+    n_ctas = args.ctas or idx.idx_recommended_decode_ctas(R, case.dtype, c.page_size, case.next_n)
     cta = torch.empty(idx.idx_schedule_ints(n_ctas), dtype=torch.int32, device="cuda")
     logits = torch.zeros((R, W), dtype=torch.float32, device="cuda")
     out = torch.empty((R, k), dtype=torch.int32, device="cuda")

@@ -117,6 +117,17 @@ int64_t idx_schedule_ints(int32_t n_ctas);
  * device once). Returns a positive count, or 0 when no device is present. */
 int32_t idx_recommended_ctas(int32_t rows);
 
+/* Work groups for idx_paged_mqa_logits on this device, by what sets the
+ * bytes each of its single-wave work groups keeps in flight: FP8 keys in
+ * 64-token blocks (pages of 64 or 256 rows) with one query row per sequence
+ * stream 8 KB blocks, and one wave per SIMD (4 per CU) keeps enough of them
+ * in flight while no two waves of a SIMD compete for issue; smaller blocks
+ * (32-row pages, MXFP4 keys) or several query rows per sequence want two
+ * waves per SIMD (8 per CU). At least `rows`. Host only; 0 when no device
+ * is present or dtype / page_size / next_n are not supported values. */
+int32_t idx_recommended_decode_ctas(int32_t rows, int32_t dtype, int32_t page_size,
+                                    int32_t next_n);
+
 /*
  * Build the decode work split (ATOM PR #1709, commit on compute_varctx_schedule:
  * one kernel writes the split straight into a fixed-address buffer that a

@@ -29,7 +29,7 @@ IDX_KIN_BF16 = 1
 
 # Every symbol include/idx.h declares.
 EXPORTS = (
-    "idx_schedule_ints", "idx_recommended_ctas", "idx_build_schedule",
+    "idx_schedule_ints", "idx_recommended_ctas", "idx_recommended_decode_ctas", "idx_build_schedule",
     "idx_paged_mqa_logits", "idx_paged_mqa_logits_varlen", "idx_varlen_windows",
     "idx_topk_workspace_size", "idx_topk",
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
     sig = {
         "idx_schedule_ints": (i64, [i32]),
         "idx_recommended_ctas": (i32, [i32]),
+        "idx_recommended_decode_ctas": (i32, [i32, i32, i32, i32]),
         "idx_build_schedule": (st, [P, i32, i32, i32, i32, P, P]),
         "idx_paged_mqa_logits": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P, i64,
                                       P, i32, i32, P, i32, P, i64, P]),
@@ -174,6 +175,10 @@ def idx_schedule_ints(n_ctas: int) -> int:
 
 def idx_recommended_ctas(rows: int) -> int:
     return load().idx_recommended_ctas(rows)
+
+
+def idx_recommended_decode_ctas(rows: int, dtype: int, page_size: int, next_n: int) -> int:
+    return load().idx_recommended_decode_ctas(rows, dtype, page_size, next_n)
 
 
 def idx_build_schedule(context_lens, B, next_n, page_size, n_ctas, cta_info, stream=None):

@@ -148,6 +148,13 @@ def test_topk_rejects_bad_arguments(lib, args, status):
     assert lib.idx_topk(*args, None) == status
 
 
+def test_recommended_decode_ctas_rejects_unsupported_values():
+    # unsupported dtype, page size or next_n give 0 before any device query
+    assert idx.idx_recommended_decode_ctas(64, 7, 64, 1) == 0
+    assert idx.idx_recommended_decode_ctas(64, 1, 48, 1) == 0
+    assert idx.idx_recommended_decode_ctas(64, 1, 64, 5) == 0
+
+
 def test_schedule_buffer_size():
     assert idx.idx_schedule_ints(512) == 2 * 513
     assert idx.idx_schedule_ints(0) == 0

@@ -74,11 +74,32 @@ def test_workload1_single_sequence_decode():
     _exact_topk_on_oracle_logits(case, [0], ref, E)
 
 
+def _bench_ctas(case):
+    """The scoring launch configuration bench.py times for this workload."""
+    n = idx.idx_recommended_decode_ctas(case.R, case.dtype, case.cache.page_size, case.next_n)
+    assert n > 0
+    return n
+
+
+def test_recommended_decode_work_groups():
+    """4 per CU for FP8 keys in 64-token blocks with one row per sequence,
+    8 per CU otherwise, at least the row count; 0 for unsupported values."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 64, 1) == 4 * cus
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 256, 1) == 4 * cus
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 32, 1) == 8 * cus
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 64, 2) == 8 * cus
+    assert idx.idx_recommended_decode_ctas(64, synth.MXFP4, 256, 1) == 8 * cus
+    assert idx.idx_recommended_decode_ctas(100000, synth.FP8, 64, 1) == 100000
+    assert idx.idx_recommended_decode_ctas(64, 7, 64, 1) == 0
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 48, 1) == 0
+
+
 def test_workload2_batched_decode_graph_replay():
     log("workload 2")
     case = synth.workload(2)
     dc = DeviceCase(case)
-    n_ctas = idx.idx_recommended_ctas(case.R)
+    n_ctas = _bench_ctas(case)
     logits, out, cnt = run_decode(dc, n_ctas=n_ctas, inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     rng = np.random.default_rng(2)
@@ -115,7 +136,7 @@ def test_workload2_batched_decode_graph_replay():
 def test_workload3_mtp_decode_page32_padded_rows():
     log("workload 3")
     case = synth.workload(3)
-    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=idx.idx_recommended_ctas(case.R),
+    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=_bench_ctas(case),
                                   inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     rng = np.random.default_rng(3)
@@ -165,7 +186,7 @@ def test_workload4_chunked_prefill():
 def test_workload5_mxfp4_decode():
     log("workload 5")
     case = synth.workload(5)
-    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=idx.idx_recommended_ctas(case.R),
+    logits, out, cnt = run_decode(DeviceCase(case), n_ctas=_bench_ctas(case),
                                   inline_split=True)
     _whole_output_properties(case, out, cnt, _decode_rows_E(case))
     rng = np.random.default_rng(5)
