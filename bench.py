@@ -684,7 +684,16 @@ def main():
         return
     if args.summarize_trace:
         d = args.summarize_trace
-        if args.sparse_attention_only:
+        if args.all_workloads:
+            summarize_trace(d, os.path.join(ROOT, "profiles", "kernels_all_decode_workloads.md"),
+                            "Kernel trace of bench.py --all-workloads: batched decode (FP8, 1 row, "
+                            "64-row pages: mqa_logits_kernel<1, 1, 4>), single-sequence decode (same "
+                            "instance), MTP decode (FP8, 2 rows, 32-row pages: <1, 2, 2>), MXFP4 decode "
+                            "(<2, 1, 4>), and the rest of the bench",
+                            "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                            "python3 -u bench.py --all-workloads --steps 20 --warmup 5 --no-cpu-baseline\n"
+                            "python3 bench.py --all-workloads --summarize-trace <dir>")
+        elif args.sparse_attention_only:
             summarize_trace(d, os.path.join(ROOT, "profiles", "sparse_mla_decode_64x2048_kernel_trace.md"),
                             "Kernel trace of the sparse attention over the selection: 64 rows x 2048 "
                             "listed tokens, 64 heads, 512-dim bf16 latent rows, page 64",
