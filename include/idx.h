@@ -405,6 +405,24 @@ idx_status idx_sparse_mla_decode(const void *q, const idx_mla_cache *kv,
                                  const int32_t *topk_lens, int32_t k, float scale, void *out,
                                  float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Opt-in device-side check of the decode contracts idx_paged_mqa_logits does
+ * not check (they need a sync to check on the host): for each sequence b,
+ * 0 <= context_lens[b] <= W (W > 0; W = 0 skips that bound) and
+ * context_lens[b] <= bt_stride*page_size, and every block_tables[b][p] of a
+ * page p holding a visible token lies in [0, num_pages). Writes int32
+ * result[4] on `stream` (device memory, no sync; read it after the stream):
+ *   result[0] sequences breaking a length bound, result[1] out-of-pool table
+ *   entries of visible pages, result[2] first such sequence, result[3]
+ *   sequence of the first such entry (each -1 when there is none).
+ * Graph-capturable (the result is cleared by a kernel, not a memset).
+ * Errors: IDX_ERR_INVALID (null or misaligned pointers, B outside
+ * [0, 16000], bt_stride, page_size, num_pages < 1, W < 0).
+ */
+idx_status idx_validate_decode(const int32_t *context_lens, int32_t B, const int32_t *block_tables,
+                               int64_t bt_stride, int32_t page_size, int64_t num_pages, int64_t W,
+                               int32_t *result, void *stream);
+
 /* Human-readable name of a status (static string). */
 const char *idx_status_string(idx_status s);
 

@@ -15,6 +15,6 @@ from .binding import (  # noqa: F401
     idx_prefill_rows_per_chunk, idx_prefill_schedule_ints, idx_prefill_scratch_bytes,
     idx_quantize_query, idx_recommended_ctas, idx_recommended_decode_ctas, idx_schedule_ints, idx_sparse_mla_decode,
     idx_sparse_mla_workspace_size, idx_topk,
-    idx_topk_workspace_size, idx_varlen_windows, idx_version,
+    idx_topk_workspace_size, idx_validate_decode, idx_varlen_windows, idx_version,
     load, make_kv_cache, make_mla_cache, make_query, ptr, stream_handle,
 )

@@ -35,7 +35,7 @@ EXPORTS = (
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
     "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_kv_cache_write",
     "idx_quantize_query", "idx_sparse_mla_workspace_size", "idx_sparse_mla_decode",
-    "idx_status_string", "idx_last_error", "idx_version",
+    "idx_validate_decode", "idx_status_string", "idx_last_error", "idx_version",
 )
 
 
@@ -110,6 +110,7 @@ def load(path: str = LIB_PATH):
         "idx_sparse_mla_workspace_size": (sz, [i32, i32]),
         "idx_sparse_mla_decode": (st, [P, ctypes.POINTER(MlaCache), P, i64, i32, i32, P, P, i32,
                                        ctypes.c_float, P, P, P, sz, P]),
+        "idx_validate_decode": (st, [P, i32, P, i64, i32, i64, i64, P, P]),
         "idx_status_string": (ctypes.c_char_p, [st]),
         "idx_last_error": (ctypes.c_char_p, []),
         "idx_version": (i32, []),
@@ -179,6 +180,13 @@ def idx_recommended_ctas(rows: int) -> int:
 
 def idx_recommended_decode_ctas(rows: int, dtype: int, page_size: int, next_n: int) -> int:
     return load().idx_recommended_decode_ctas(rows, dtype, page_size, next_n)
+
+
+def idx_validate_decode(context_lens, B, block_tables, bt_stride, page_size, num_pages, W, result,
+                        stream=None):
+    _check(load().idx_validate_decode(ptr(context_lens), B, ptr(block_tables), bt_stride, page_size,
+                                      num_pages, W, ptr(result), stream_handle(stream)),
+           "idx_validate_decode")
 
 
 def idx_build_schedule(context_lens, B, next_n, page_size, n_ctas, cta_info, stream=None):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libidx.so")
 SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip", "kv_write.hip",
-           "q_quant.hip", "sparse_mla.hip"]
+           "q_quant.hip", "sparse_mla.hip", "validate.hip"]
 ARCH = "gfx950"
 
 

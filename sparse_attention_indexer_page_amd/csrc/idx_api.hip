@@ -161,6 +161,34 @@ int32_t idx_recommended_ctas(int32_t rows) {
   return (int32_t)(n < kMaxCtas ? n : kMaxCtas);
 }
 
+idx_status idx_validate_decode(const int32_t *context_lens, int32_t B, const int32_t *block_tables,
+                               int64_t bt_stride, int32_t page_size, int64_t num_pages, int64_t W,
+                               int32_t *result, void *stream) {
+  if (!context_lens || !block_tables || !result)
+    return fail(IDX_ERR_INVALID, "null context_lens, block_tables or result");
+  if (B < 0 || B > idx::kMaxSegs) return fail(IDX_ERR_INVALID, "B = %d outside [0, %d]", B, idx::kMaxSegs);
+  if (bt_stride < 1 || bt_stride > (1 << 30))
+    return fail(IDX_ERR_INVALID, "bt_stride %lld outside [1, 2^30]", (long long)bt_stride);
+  if (!valid_page_size(page_size))
+    return fail(IDX_ERR_INVALID, "page_size %d not in {32, 64, 256}", page_size);
+  if (num_pages < 1 || W < 0) return fail(IDX_ERR_INVALID, "num_pages must be >= 1 and W >= 0");
+  if (!aligned(result, 4) || !aligned(context_lens, 4) || !aligned(block_tables, 4))
+    return fail(IDX_ERR_INVALID, "context_lens, block_tables and result must be 4-byte aligned");
+  idx::ValidateArgs a;
+  a.lens = context_lens;
+  a.B = B;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.bt_cols = (int32_t)bt_stride; // the decode scores read up to bt_stride entries per row
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.W = W;
+  a.result = result;
+  hipError_t e = idx::launch_validate_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "validation launch");
+  return ok();
+}
+
 int32_t idx_recommended_decode_ctas(int32_t rows, int32_t dtype, int32_t page_size,
                                     int32_t next_n) {
   if ((dtype != IDX_FP8_E4M3 && dtype != IDX_MXFP4) || !valid_page_size(page_size) ||

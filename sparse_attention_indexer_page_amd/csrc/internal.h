@@ -152,7 +152,20 @@ struct MlaArgs {
   float *lse;     // [R][64] or null
 };
 
+struct ValidateArgs {
+  const int32_t *lens;         // [B]
+  int32_t B;
+  const int32_t *block_tables; // [B][bt_stride]
+  int64_t bt_stride;
+  int32_t bt_cols;             // entries per row the scores may read
+  int32_t page_size;
+  int64_t num_pages;
+  int64_t W;                   // logits width, or 0: not checked
+  int32_t *result;             // [4]
+};
+
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+hipError_t launch_validate_decode(const ValidateArgs &a, hipStream_t s);
 hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t s);
 hipError_t launch_fill_tail(const int32_t *lens, const int32_t *row_offsets, int32_t B, int32_t n,

@@ -186,6 +186,19 @@ def test_prefill_chunk_rule_reproduces_the_pages_buffer_sizes():
     assert idx.idx_prefill_rows_per_chunk(4096, 1) == 1
 
 
+@pytest.mark.parametrize("args,want", [
+    ((0, 4, 0x200, 8, 64, 10, 100, 0x300), "INVALID"),          # null lens
+    ((0x100, 4, 0x200, 8, 48, 10, 100, 0x300), "INVALID"),      # page size
+    ((0x100, 16001, 0x200, 8, 64, 10, 100, 0x300), "INVALID"),  # B
+    ((0x100, 4, 0x200, 0, 64, 10, 100, 0x300), "INVALID"),      # bt_stride
+    ((0x100, 4, 0x200, 8, 64, 0, 100, 0x300), "INVALID"),       # num_pages
+    ((0x100, 4, 0x200, 8, 64, 10, -1, 0x300), "INVALID"),       # W
+    ((0x100, 4, 0x200, 8, 64, 10, 100, 0x302), "INVALID"),      # result alignment
+])
+def test_validate_decode_rejects_bad_arguments(lib, args, want):
+    assert lib.idx_validate_decode(*args, None) == getattr(idx, "IDX_ERR_" + want)
+
+
 def test_prefill_rejects_small_scratch(lib):
     q, kv = _q(), _kv()
     rc = lib.idx_prefill_chunked_topk(ctypes.byref(q), ctypes.byref(kv), 0x100, 0x200, 64, 256,
