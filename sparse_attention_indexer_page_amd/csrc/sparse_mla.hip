@@ -30,7 +30,10 @@
 //     k-slots 8g..8g+7 = tokens 4g..4g+3 of both tiles), so P needs no
 //     shuffle, only bf16 rounding;
 //   * O += P V on v_mfma_f32_16x16x32_bf16 (heads x 16 dims, K = the 32
-//     tokens), 16 tiles for the wave's 256 dims, fp32 accumulators in VGPRs.
+//     tokens), 16 tiles for the wave's 256 dims, fp32 accumulators in VGPRs;
+//     a lane reads 8-byte runs of 4 dims per token and byte-permutes them
+//     into the token-major B operands of 4 tiles (a tile's 16 columns are
+//     then every fourth dim), rather than reading 2-byte columns.
 // Each chunk leaves (max, sum, unnormalized O) per head in the workspace; a
 // second launch merges the chunks of every (row, head) and writes bf16 out
 // and the log-sum-exp.
@@ -82,7 +85,7 @@ __device__ inline float rows_sum(float v) {
 
 struct MlaState {
   v8bf qb[kWaveDims / 32]; // head col of the wave's group, dims 256 dh + 32 kk + 8 g .. + 8
-  v4f O[kWaveDims / 16]; // heads 4g + jj, dims 16 dt + col of the wave's half
+  v4f O[kWaveDims / 16]; // heads 4g + jj; tile 4 p + j: dims 64 p + 4 col + j of the wave's half
   float m_run, l_run;    // head col of the wave's group
 };
 
@@ -155,18 +158,33 @@ __device__ inline void score_block(const MlaArgs &a, MlaState &S, const uint8_t 
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     pa[i] = __builtin_bit_cast(__bf16, (uint16_t)bf16_rne(p[i >> 2][i & 3]));
-  const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile) + kWaveDims * dh;
+  // V operands: lane col reads 8 bytes (dims 4 col .. + 3 of a 64-dim
+  // span) of each of its 8 tokens and regroups them into the B operands of
+  // four tiles, tile j taking dim 4 col + j of every token (two tokens per
+  // dword, by byte permutes)
+  const uint8_t *tv = tile + 2 * kWaveDims * dh + 8 * col;
 #pragma unroll
-  for (int dt = 0; dt < kWaveDims / 16; ++dt) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) S.O[dt][jj] *= ah[jj];
-    v8bf vb;
+  for (int p4 = 0; p4 < kWaveDims / 64; ++p4) {
+    uint2 w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      vb[i] = __builtin_bit_cast(__bf16, t16[(pv_token(g, i) * kTileRow) / 2 + 16 * dt + col]);
-    S.O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, S.O[dt], 0, 0, 0);
-    // keep the V reads of at most two tiles in flight
-    if ((dt & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+      w[i] = *reinterpret_cast<const uint2 *>(tv + pv_token(g, i) * kTileRow + 128 * p4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      v4i vb;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = (j & 2) ? w[2 * m].y : w[2 * m].x;
+        const uint32_t hi = (j & 2) ? w[2 * m + 1].y : w[2 * m + 1].x;
+        vb[m] = (int)__builtin_amdgcn_perm(hi, lo, sel);
+      }
+      v4f &o = S.O[4 * p4 + j];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) o[jj] *= ah[jj];
+      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(v8bf, vb), o, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0); // the V reads of one 64-dim span in flight
   }
 }
 
@@ -267,11 +285,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_partial_kernel(MlaArgs a)
 
   // ---- this chunk's (max, sum, unnormalized O) per head
   const int64_t base = ((int64_t)r * a.nsplit + sp) * kMlaHeads + 16 * hg;
+  // tile 4 p + j holds dims 64 p + 4 col + j of the wave's half
 #pragma unroll
-  for (int dt = 0; dt < kWaveDims / 16; ++dt)
+  for (int p4 = 0; p4 < kWaveDims / 64; ++p4)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-      a.ws_o[(base + 4 * g + jj) * kMlaDim + kWaveDims * dh + 16 * dt + col] = S.O[dt][jj];
+      *reinterpret_cast<v4f *>(a.ws_o + (base + 4 * g + jj) * kMlaDim + kWaveDims * dh + 64 * p4 +
+                               4 * col) =
+          v4f{S.O[4 * p4][jj], S.O[4 * p4 + 1][jj], S.O[4 * p4 + 2][jj], S.O[4 * p4 + 3][jj]};
   if (g == 0 && dh == 0) {
     a.ws_ml[(base + col) * 2] = S.m_run;
     a.ws_ml[(base + col) * 2 + 1] = S.l_run;
