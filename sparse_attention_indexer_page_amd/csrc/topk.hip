@@ -117,6 +117,26 @@ __device__ __forceinline__ uint32_t first_key_in_bin_at_least(uint32_t lo, uint3
   return hi;
 }
 
+// The same search, first tried over the 64 keys just below and above
+// `guess` (a key computed to lie near the answer): the narrower interval is
+// taken only where the bins at its ends confirm that it holds the answer,
+// so the result is the same, in one round instead of up to six.
+template <typename BinOf>
+__device__ __forceinline__ uint32_t first_key_in_bin_near(uint32_t lo, uint32_t hi, uint32_t b,
+                                                         uint32_t guess, BinOf bin_of) {
+  constexpr uint32_t kHalf = 32u;
+  if (guess > lo + kHalf && guess - kHalf < hi && bin_of(guess - kHalf) < b) lo = guess - kHalf;
+  if (hi > kHalf && guess < hi - kHalf && guess + kHalf > lo && bin_of(guess + kHalf) >= b)
+    hi = guess + kHalf;
+  return first_key_in_bin_at_least(lo, hi, b, bin_of);
+}
+
+// A key near the lower edge of value bin b under the linear map
+// bin = (x / 2 - h0) * scale (the edge's value, rounded).
+__device__ inline uint32_t bin_edge_key(uint32_t b, float h0, float scale) {
+  return float_key(((float)b / scale + h0) * 2.0f);
+}
+
 constexpr int kCandCap = 4096; // keys of the first pass's bin refined in LDS
 
 constexpr int kRankCap = 64; // candidates ranked directly by one wave
@@ -280,9 +300,9 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
     // the key); every wave finds its ends from the uniform kmin, kmax and bin
     // alike, so no pass over the keys and no barrier. The bin is not empty,
     // so its first key is <= kmax and has bin exactly `bin`.
-    lo = first_key_in_bin_at_least(kmin - 1u, kmax, bin, vbin);
+    lo = first_key_in_bin_near(kmin - 1u, kmax, bin, bin_edge_key(bin, h0, scale), vbin);
     hi = bin + 1 < (uint32_t)kBins && vbin(kmax) > bin
-             ? first_key_in_bin_at_least(lo, kmax, bin + 1, vbin) - 1u
+             ? first_key_in_bin_near(lo, kmax, bin + 1, bin_edge_key(bin + 1, h0, scale), vbin) - 1u
              : kmax;
     if (inbin == need) {
       thr = lo - 1u; // lo >= kmin > 0
@@ -641,9 +661,9 @@ __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, 
     need -= above;
     cand = inbin;
     // the bin's keys form the key interval [lo, hi] (see the block kernel)
-    lo = first_key_in_bin_at_least(kmin - 1u, kmax, bin, vbin);
+    lo = first_key_in_bin_near(kmin - 1u, kmax, bin, bin_edge_key(bin, h0, scale), vbin);
     hi = bin + 1 < (uint32_t)kWaveBins && vbin(kmax) > bin
-             ? first_key_in_bin_at_least(lo, kmax, bin + 1, vbin) - 1u
+             ? first_key_in_bin_near(lo, kmax, bin + 1, bin_edge_key(bin + 1, h0, scale), vbin) - 1u
              : kmax;
     if (inbin == need) {
       thr = lo - 1u; // lo >= kmin > 0
