@@ -612,6 +612,26 @@ def sparse_mla_bench(args, torch, idx, synth):
             "bf16_tflops": flops / (ms * 1e-3) / 1e12, "workspace_bytes": wsb}
 
 
+def host_cpu():
+    """The host the CPU baseline ran on: logical CPUs, the ones this process
+    may use, and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(case, budget_s):
     """The CPU oracle on a bounded sample of the decode workload: groups of
     rows in a fixed random order, cycling over the workload's rows, until
@@ -646,6 +666,7 @@ def cpu_baseline(case, budget_s):
         "unit": "tokens/s",
         "cores": oracle.threads(),
         "kind": "oracle",
+        "host": host_cpu(),
         "sample": "%d row evaluations cycling over the %d decode rows (%d scored tokens, "
                   "logits + top-k), %.1f s" % (len(done), case.R, tokens, elapsed),
     }
@@ -735,10 +756,9 @@ def main():
 
     import synth
     import sparse_attention_indexer_page_amd as idx
-    from sparse_attention_indexer_page_amd import binding, build
+    from sparse_attention_indexer_page_amd import build
 
-    if not os.path.exists(binding.LIB_PATH):
-        build.build()
+    build.ensure_built()  # rebuilds when a source changed since the last build
     idx.load()
     torch.cuda.set_device(0)
 

@@ -167,9 +167,10 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
  *                  which ATOM PR #1709 says a passed cta_info skips), saving
  *                  the builder launch
  *   logits         fp32 [B*next_n][W]
- * Errors: IDX_ERR_INVALID (null pointer, shape, alignment, W < 1, cta_info
- * NULL with B > 1024), IDX_ERR_UNSUPPORTED (H != 64, D != 128, dtype
- * mismatch).
+ * Errors: IDX_ERR_INVALID (null pointer, shape, alignment, W outside
+ * [1, 2^22], cta_info NULL with B > 1024), IDX_ERR_UNSUPPORTED (H != 64,
+ * D != 128, dtype mismatch). Work is split by lengths clamped to 2^22 tokens,
+ * so a length breaking the contract len <= W cannot overflow the split.
  */
 idx_status idx_paged_mqa_logits(const idx_query *q, const idx_kv_cache *kv,
                                 const int32_t *block_tables, int64_t bt_stride,

@@ -18,7 +18,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 builds and loads a copy instrumented with AddressSanitizer
+# and UndefinedBehaviorSanitizer (every report fatal); the process must then
+# preload gcc's libasan and libubsan (the interpreter itself is not built with
+# them).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE", "") not in ("", "0")
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 
 FP8 = 1
 MXFP4 = 2
@@ -32,6 +37,9 @@ def build(force: bool = False) -> str:
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
                "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        if _SANITIZE:
+            cmd[1:1] = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                        "-fno-omit-frame-pointer", "-g"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -7,6 +7,7 @@ VGPRs (the fused epilogue reads every accumulator).
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -19,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libidx.so")
+# digest of the sources and flags the library at LIB was built from
+DIGEST = LIB + ".digest"
 SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip", "kv_write.hip",
            "q_quant.hip", "sparse_mla.hip", "validate.hip"]
 ARCH = "gfx950"
@@ -53,8 +56,40 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def source_digest() -> str:
+    """SHA-256 over every file under csrc/ and include/, this script and the
+    compiler flags: what the library's bits depend on."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))]
+    files += [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE))]
+    files.append(os.path.abspath(__file__))
+    for path in files:
+        if os.path.isfile(path):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+    h.update(" ".join(_flags()).encode())
+    return h.hexdigest()
+
+
+def up_to_date() -> bool:
+    """True when libidx.so exists and was built from the current sources."""
+    if not os.path.exists(LIB) or not os.path.exists(DIGEST):
+        return False
+    with open(DIGEST) as fh:
+        return fh.read().strip() == source_digest()
+
+
+def ensure_built(verbose: bool = False) -> str:
+    """Builds libidx.so unless it was built from the current sources."""
+    if not up_to_date():
+        build(verbose)
+    return LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libidx.so; returns the library path."""
+    digest = source_digest()
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
@@ -66,6 +101,9 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError("linking libidx.so failed:\n%s%s" % (res.stdout, res.stderr))
     os.replace(tmp, LIB)
+    with open(DIGEST + ".tmp%d" % os.getpid(), "w") as fh:
+        fh.write(digest + "\n")
+    os.replace(DIGEST + ".tmp%d" % os.getpid(), DIGEST)
     return LIB
 
 

@@ -256,7 +256,8 @@ idx_status decode_logits(const idx_query *q, const idx_kv_cache *kv, const int32
   if (bt_stride < 1) return fail(IDX_ERR_INVALID, "bt_stride must be >= 1");
   if (n_ctas < 1 || n_ctas > kMaxCtas)
     return fail(IDX_ERR_INVALID, "n_ctas = %d outside [1, %d]", n_ctas, kMaxCtas);
-  if (W < 1 || W > (1ll << 31)) return fail(IDX_ERR_INVALID, "W = %lld outside [1, 2^31]", (long long)W);
+  if (W < 1 || W > idx::kMaxSegLen)
+    return fail(IDX_ERR_INVALID, "W = %lld outside [1, 2^22]", (long long)W);
   idx::LogitsArgs a = logits_args(q, kv);
   a.block_tables = block_tables;
   a.bt_stride = bt_stride;

@@ -15,6 +15,14 @@ constexpr int kTile = 16;    // tokens per MFMA column tile
 constexpr int kInlineSplitMaxSegs = 1024; // decode without a schedule buffer: B at most this
 constexpr int kMaxSegs = 16000;      // schedule segments the builder scans in LDS (64000 B)
 constexpr int kTopkMaxW = 65536;     // in-register top-k row capacity
+// Longest segment the work split counts blocks for: every length is clamped
+// to this before its blocks are counted, so kMaxSegs segments of 32-token
+// blocks sum to less than 2^31 units and no split arithmetic overflows, even
+// for lengths that break the device contract (len <= W <= kMaxSegLen).
+constexpr int32_t kMaxSegLen = 1 << 22;
+__host__ __device__ inline int32_t clamp_seg_len(int32_t v) {
+  return v < 0 ? 0 : (v > kMaxSegLen ? kMaxSegLen : v);
+}
 constexpr int kPrefillRowsPerSeg = 7;  // query rows sharing one K stream in prefill
 // Work-split cost of entering a segment, in key blocks: a prefill row block
 // reloads seven query rows (about one block's scoring time); a decode

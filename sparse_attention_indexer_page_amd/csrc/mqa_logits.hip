@@ -134,8 +134,7 @@ __device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows
 
 // Length of sequence s (its last row's visible length).
 __device__ inline int32_t segment_length(const LogitsArgs &a, int s) {
-  const int32_t v = uniform_load(a.lens + s);
-  return v > 0 ? v : 0;
+  return clamp_seg_len(uniform_load(a.lens + s));
 }
 
 // Position of a wave in its work group's range of (segment, block) items.
@@ -192,13 +191,13 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   int32_t len[kChunks];
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) // every load first: one round trip
-    if (i * 64 < a.nseg) len[i] = 64 * i + lane < a.nseg ? a.lens[64 * i + lane] : 0;
+    if (i * 64 < a.nseg) len[i] = 64 * i + lane < a.nseg ? clamp_seg_len(a.lens[64 * i + lane]) : 0;
   int32_t pre[kChunks]; // exclusive prefix cost of sequence 64 i + lane
   int32_t total = 0;
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
     if (i * 64 < a.nseg) {
-      const int32_t L = len[i] > 0 ? len[i] : 0;
+      const int32_t L = len[i]; // clamped to [0, kMaxSegLen]
       const int32_t nb = (L + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens); // 32 or 64
       const int32_t cost = nb > 0 ? nb + kDecodeEntryCost : 0;
       const int32_t incl = wave_incl_scan(cost);
@@ -242,7 +241,7 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
       w.be = blk;
     }
   }
-  return len0 > 0 ? len0 : 0;
+  return len0;
 }
 
 // K operands of one block: TPB tiles of 16 tokens of one page.

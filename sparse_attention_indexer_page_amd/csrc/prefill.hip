@@ -83,7 +83,7 @@ __device__ inline int32_t block_length(const LogitsArgs &a, int s) {
       L = e > L ? e : L;
     }
   }
-  return L;
+  return clamp_seg_len(L);
 }
 
 __device__ inline bool in_range(const LogitsArgs &a, const Walk &w) {

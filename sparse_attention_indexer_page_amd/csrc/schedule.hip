@@ -28,10 +28,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
 __device__ inline int32_t segment_length(const ScheduleArgs &a, int s) {
-  if (a.mode == kSegDecode) {
-    int32_t v = a.lens[s];
-    return v > 0 ? v : 0;
-  }
+  if (a.mode == kSegDecode) return clamp_seg_len(a.lens[s]);
   int32_t m = 0;
   const int r0 = a.row0 + s * kPrefillRowsPerSeg;
 #pragma unroll
@@ -42,7 +39,7 @@ __device__ inline int32_t segment_length(const ScheduleArgs &a, int s) {
       m = v > m ? v : m;
     }
   }
-  return m;
+  return clamp_seg_len(m);
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {

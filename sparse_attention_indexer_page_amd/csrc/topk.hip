@@ -239,14 +239,16 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   // ---- keys (0 past the row: every visible key is > 0x007FFFFF)
   uint32_t key[IPT];
   // Loads through a buffer resource bounded by the row's E scores: past the
-  // row they return 0 without a predicate; such items then get key 0.
+  // row they return 0 without a predicate and touch no memory; such items
+  // then get key 0. The item step is part of the vector offset, which the
+  // hardware checks against the bound (the scalar offset is not checked).
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(row), (short)0, E * 4, 0x00020000);
   const uint32_t voff = (uint32_t)(base + lane) * 4u;
   const int left = E - base - lane; // item i is visible iff 64 * i < left
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
-    const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, voff, 256 * i, 0);
+    const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, voff + 256u * i, 0, 0);
     key[i] = (i < rounds && 64 * i < left) ? float_key(__uint_as_float(bits)) : 0u;
   }
   if (tid == 0) {
@@ -619,8 +621,9 @@ __device__ __forceinline__ void select_row_wave(const float *row, int E, int k, 
   uint32_t key[IPT]; // item i holds index 64 i + lane; 0 past the row
   const int left = E - lane;
 #pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)lane * 4u, 256 * i, 0);
+  for (int i = 0; i < IPT; ++i) { // bounded like the block kernel's loads
+    const uint32_t bits =
+        __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)lane * 4u + 256u * i, 0, 0);
     key[i] = 64 * i < left ? float_key(__uint_as_float(bits)) : 0u;
   }
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;

@@ -23,9 +23,10 @@ def log(msg):
 
 
 def ensure_built():
-    from sparse_attention_indexer_page_amd import binding, build
-    if not os.path.exists(binding.LIB_PATH):
-        build.build()
+    """Builds libidx.so when its sources changed since the last build, then
+    loads it."""
+    from sparse_attention_indexer_page_amd import build
+    build.ensure_built()
     idx.load()
 
 

@@ -17,9 +17,8 @@ HEADER = os.path.join(ROOT, "include", "idx.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(binding.LIB_PATH):
-        from sparse_attention_indexer_page_amd import build
-        build.build()
+    from sparse_attention_indexer_page_amd import build
+    build.ensure_built()
     return idx.load()
 
 
@@ -116,7 +115,8 @@ def test_logits_rejects_bad_cache(lib, mutate, status):
     (dict(B=0), idx.IDX_ERR_INVALID), (dict(B=16001), idx.IDX_ERR_INVALID),
     (dict(cta=0, B=1025), idx.IDX_ERR_INVALID),  # no schedule buffer: B <= 1024 only
     (dict(nc=0), idx.IDX_ERR_INVALID),
-    (dict(W=0), idx.IDX_ERR_INVALID), (dict(bts=0), idx.IDX_ERR_INVALID),
+    (dict(W=0), idx.IDX_ERR_INVALID), (dict(W=(1 << 22) + 1), idx.IDX_ERR_INVALID),
+    (dict(bts=0), idx.IDX_ERR_INVALID),
 ])
 def test_logits_rejects_bad_shapes(lib, kw, status):
     assert _logits(_q(), _kv(), **kw) == status
@@ -329,3 +329,46 @@ def test_sparse_mla_rejects_bad_arguments(lib):
     assert call(wsb=16) == idx.IDX_ERR_WORKSPACE
     assert idx.idx_sparse_mla_workspace_size(2, 16) == 2 * 1 * 64 * 514 * 4
     assert idx.idx_sparse_mla_workspace_size(0, 16) == 0
+
+
+def _topk_loads(E, NT, IPT, wave_kernel):
+    """The top-k kernels' row loads as (byte offset, read by the kernel)
+    pairs: the block kernel gives wave w of NT/64 the indices
+    [w*rounds*64, ...), lane l of item i index base + 64 i + l, and keeps the
+    item iff i < rounds and 64 i < E - base - l; the one-wave kernel keeps
+    item i of lane l iff 64 i < E - l. The byte offset is the load's vector
+    offset (the item step folded in), which the buffer bound of E*4 bytes
+    checks."""
+    loads = []
+    NW = 1 if wave_kernel else NT // 64
+    rounds = IPT if wave_kernel else (E + NW * 64 - 1) // (NW * 64)
+    for w in range(NW):
+        base = w * rounds * 64
+        for lane in range(64):
+            left = E - base - lane
+            for i in range(IPT):
+                off = (base + lane) * 4 + 256 * i
+                keep = (64 * i < left) if wave_kernel else (i < rounds and 64 * i < left)
+                loads.append((off, keep))
+    return loads
+
+
+@pytest.mark.parametrize("wave_kernel,NT,buckets", [
+    (False, 1024, [(4, 4096), (8, 8192), (16, 16384), (32, 32768), (64, 65536)]),
+    (True, 64, [(16, 1024), (32, 2048), (64, 4096)]),
+])
+def test_topk_row_loads_stay_inside_the_row(wave_kernel, NT, buckets):
+    """Every load the top-k kernels keep lies inside the row's E scores, so
+    every load past the row (offset >= E*4, which the buffer bound turns into
+    a zero without touching memory) is one the kernel discards; the kept
+    loads cover each index below E exactly once."""
+    for IPT, max_e in buckets:
+        for E in sorted({1, 63, 64, 65, max_e // 2 + 1, max_e - 1, max_e}):
+            if E < 1 or E > max_e:
+                continue
+            seen = [0] * E
+            for off, keep in _topk_loads(E, NT, IPT, wave_kernel):
+                if keep:
+                    assert off + 4 <= 4 * E, (IPT, E, off)
+                    seen[off // 4] += 1
+            assert all(c == 1 for c in seen), (IPT, E)

@@ -193,8 +193,9 @@ def _adversarial_rows(W, rng):
 @pytest.mark.parametrize("E,k", [(65, 64), (1000, 1), (1000, 999), (1500, 700), (2049, 2048),
                                  (3000, 2048), (4096, 2048), (4096, 4095)])
 def test_topk_short_rows_exact(E, k):
-    """Widths up to 4096 take the one-wave-per-row selection: exact against
-    the oracle's top-k of the same fp32 values on adversarial rows."""
+    """A few rows of width 4096 (fewer than 2048 rows: the one-work-group-per-
+    row selection): exact against the oracle's top-k of the same fp32 values
+    on adversarial rows."""
     W = 4096
     rng = np.random.default_rng(E * 7 + k)
     rows = _adversarial_rows(W, rng)
@@ -208,6 +209,41 @@ def test_topk_short_rows_exact(E, k):
     assert torch.all(cnt.cpu() == min(k, E))
     for r in range(len(rows)):
         check_topk_exact(out[r].cpu().numpy(), vals[r], E, k, "E=%d k=%d row %d" % (E, k, r))
+
+
+@pytest.mark.parametrize("k", [1, 64, 700, 999, 2048, 4095])
+def test_topk_wave_kernel_adversarial_rows_exact(k):
+    """2560 rows of width 4096 (>= 2048 rows: one wave per row): the five
+    adversarial row families at lengths in each of the kernel's three key
+    buckets (<= 1024, <= 2048, <= 4096 keys), plus rows no longer than k;
+    every row exact against the oracle's top-k of the same fp32 values."""
+    log("topk wave kernel k %d" % k)
+    W, R = 4096, 2560
+    rng = np.random.default_rng(4242 + k)
+    buckets = [(k + 1, 1024), (max(k + 1, 1025), 2048), (max(k + 1, 2049), 4096)]
+    buckets = [(lo, hi) for lo, hi in buckets if lo <= hi]
+    vals = np.empty((R, W), dtype=np.float32)
+    E = np.empty(R, dtype=np.int32)
+    fams = None
+    for r in range(R):
+        if r % 5 == 0:
+            fams = _adversarial_rows(W, rng)
+        vals[r] = fams[r % 5]
+        if r % 17 == 16:  # everything visible is selected
+            E[r] = rng.integers(0, k + 1)
+        else:
+            lo, hi = buckets[(r // 5) % len(buckets)]
+            E[r] = rng.integers(lo, hi + 1)
+    dev = torch.from_numpy(vals).cuda()
+    lens = torch.from_numpy(E).cuda()
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(R, dtype=torch.int32, device="cuda")
+    idx.idx_topk(dev, W, lens, R, 1, k, out, cnt)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(cnt.cpu().numpy(), np.minimum(E, k))
+    for r in range(R):
+        check_topk_exact(o[r], vals[r], int(E[r]), k, "k=%d row %d (E=%d)" % (k, r, E[r]))
 
 
 def test_topk_all_equal_and_two_values():
