@@ -347,7 +347,7 @@ FP8_MFMA_FLOPS = 16 * 16 * 128 * 2  # one v_mfma_f32_16x16x128_f8f6f4
 
 def prefill_source_digest():
     h = hashlib.sha256()
-    for f in ("prefill.hip", "device_common.h", "internal.h"):
+    for f in ("mqa_logits.hip", "device_common.h", "internal.h"):
         with open(os.path.join(ROOT, "sparse_attention_indexer_page_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

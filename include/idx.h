@@ -434,7 +434,9 @@ const char *idx_last_error(void);
  * the K-cache writer, the query quantizer, ragged decode, the prefill
  * index_base argument, query flags and decode without a schedule buffer;
  * 0.3.0 adds the sparse attention over the selection and spreads prefill rows
- * evenly over the chunks the budget requires. */
+ * evenly over the chunks the budget requires; 0.4.0 limits the decode width
+ * to 2^22 and sizes prefill schedules for two-row segments
+ * (idx_prefill_schedule_ints). */
 int32_t idx_version(void);
 
 #ifdef __cplusplus

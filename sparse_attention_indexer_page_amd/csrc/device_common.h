@@ -30,13 +30,14 @@ __device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// max(x, 0) as a signed-integer max of the IEEE bits: non-negative floats
-// (and +0) keep their bits, every negative float (and -0) becomes +0. One
-// integer op, with none of the NaN canonicalization a float max carries.
-__device__ inline float relu(float x) {
-  const int b = __float_as_int(x);
-  return __int_as_float(b > 0 ? b : 0);
-}
+// 2 * max(x, 0), exactly: x + |x| is 2x for x > 0 and +0 otherwise, and
+// doubling is exact. One add with an abs source modifier, a full-rate VALU
+// op on gfx950, where an integer or float max issues at about half that rate
+// (measured: 1.1 vs 1.8 ns per wave64 op per SIMD). The scoring epilogues
+// sum w * relu2(s) and halve the head sum once per token, which gives the
+// same bits as summing w * max(s, 0): every partial sum is exactly twice as
+// large (barring overflow and subnormal results).
+__device__ inline float relu2(float x) { return x + __builtin_fabsf(x); }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // of the wave are outstanding (gfx9 layout: vmcnt in bits [3:0] and [15:14];

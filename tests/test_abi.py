@@ -178,10 +178,11 @@ def test_prefill_chunk_rule_reproduces_the_pages_buffer_sizes():
     assert idx.idx_prefill_scratch_bytes(T, 4096, 256_000_000) == 4 * 4096 * 8192
     # Uneven counts: 3 chunks of at most 5 rows for 11 rows -> 4 rows each.
     assert idx.idx_prefill_scratch_bytes(11, 4096, 4 * 4096 * 5) == 4 * 4096 * 4
-    # One schedule per chunk, each for min(512, ceil(rows / 7)) work groups.
-    assert idx.idx_prefill_schedule_ints(T, 4096, 256_000_000) == 2 * idx.idx_schedule_ints(512)
+    # One schedule per chunk, each for min(1024, ceil(rows / 2)) work groups.
+    assert idx.idx_prefill_schedule_ints(T, 4096, 256_000_000) == 2 * idx.idx_schedule_ints(1024)
     assert idx.idx_prefill_schedule_ints(5, 4096, 1) == 5 * idx.idx_schedule_ints(1)
-    assert idx.idx_prefill_schedule_ints(T, 4096, big) == idx.idx_schedule_ints(512)
+    assert idx.idx_prefill_schedule_ints(T, 4096, big) == idx.idx_schedule_ints(1024)
+    assert idx.idx_prefill_schedule_ints(1000, 4096, big) == idx.idx_schedule_ints(500)
     # One row per chunk at a budget below one row.
     assert idx.idx_prefill_rows_per_chunk(4096, 1) == 1
 
