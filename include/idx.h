@@ -291,6 +291,42 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
                                     int64_t scratch_bytes, int32_t *cta_scratch,
                                     int64_t cta_scratch_ints, int32_t *out_idx, void *stream);
 
+/* Capacity of the fixed device scratch of idx_prefill_chunked_topk_noalloc:
+ * fp32 logits bytes and schedule int32 entries, one copy per GPU. */
+#define IDX_NOALLOC_LOGITS_BYTES (64ll << 20)
+#define IDX_NOALLOC_SCHEDULE_INTS (1ll << 18)
+
+/*
+ * idx_prefill_chunked_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same scores and selection, with the two scratch buffers
+ * (the chunk's fp32 logits and every chunk's schedule) taken from a fixed
+ * array in the library's own device memory instead of from the caller. The
+ * array (IDX_NOALLOC_LOGITS_BYTES + 4 * IDX_NOALLOC_SCHEDULE_INTS bytes,
+ * 65 MiB) exists once per GPU the library runs on and is held until the
+ * process ends; the call makes no allocation. Its address on the current
+ * device is looked up on the first call on that device (one
+ * hipGetSymbolAddress; make that first call outside graph capture).
+ *   Arguments as idx_prefill_chunked_topk without the scratch buffers.
+ *   budget_bytes is capped at IDX_NOALLOC_LOGITS_BYTES; the selection does
+ *   not depend on the budget, so out_idx is identical to what
+ *   idx_prefill_chunked_topk writes for the same inputs.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialized by the
+ * caller. Nothing in the array needs to start at zero (every entry is
+ * written before it is read), so no call clears it.
+ * Errors: those of idx_prefill_chunked_topk; IDX_ERR_WORKSPACE when the
+ * chunk plan for T and W under the capped budget needs more than the fixed
+ * scratch holds (more than IDX_NOALLOC_SCHEDULE_INTS schedule entries; e.g.
+ * more than about 260000 rows at W = 65536), checked on the host before any
+ * HIP call.
+ */
+idx_status idx_prefill_chunked_topk_noalloc(const idx_query *q, const idx_kv_cache *kv,
+                                            const int32_t *block_table,
+                                            const int32_t *visible_end, int32_t T, int64_t W,
+                                            int64_t budget_bytes, int32_t k, int32_t index_base,
+                                            int32_t *out_idx, void *stream);
+
 /* Element type of the rows idx_kv_cache_write and idx_quantize_query
  * quantize. */
 typedef enum idx_kin_dtype {
@@ -434,9 +470,9 @@ const char *idx_last_error(void);
  * the K-cache writer, the query quantizer, ragged decode, the prefill
  * index_base argument, query flags and decode without a schedule buffer;
  * 0.3.0 adds the sparse attention over the selection and spreads prefill rows
- * evenly over the chunks the budget requires; 0.4.0 limits the decode width
- * to 2^22 and sizes prefill schedules for two-row segments
- * (idx_prefill_schedule_ints). */
+ * evenly over the chunks the budget requires; 0.4.0 adds
+ * idx_prefill_chunked_topk_noalloc, limits the decode width to 2^22 and
+ * sizes prefill schedules for two-row segments (idx_prefill_schedule_ints). */
 int32_t idx_version(void);
 
 #ifdef __cplusplus

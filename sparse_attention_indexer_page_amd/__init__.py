@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     KVCache, MlaCache, Query,
     idx_build_schedule, idx_kv_cache_write,
     idx_last_error_message, idx_paged_mqa_logits, idx_paged_mqa_logits_varlen,
-    idx_prefill_chunked_topk,
+    idx_prefill_chunked_topk, idx_prefill_chunked_topk_noalloc,
     idx_prefill_rows_per_chunk, idx_prefill_schedule_ints, idx_prefill_scratch_bytes,
     idx_quantize_query, idx_recommended_ctas, idx_recommended_decode_ctas, idx_schedule_ints, idx_sparse_mla_decode,
     idx_sparse_mla_workspace_size, idx_topk,

@@ -24,6 +24,10 @@ IDX_FP8_E4M3 = 1
 IDX_MXFP4 = 2
 
 IDX_QUERY_FILL_NEG_INF = 1
+
+# capacity of the fixed scratch of idx_prefill_chunked_topk_noalloc
+IDX_NOALLOC_LOGITS_BYTES = 64 << 20
+IDX_NOALLOC_SCHEDULE_INTS = 1 << 18
 IDX_KIN_F32 = 0
 IDX_KIN_BF16 = 1
 
@@ -33,7 +37,8 @@ EXPORTS = (
     "idx_paged_mqa_logits", "idx_paged_mqa_logits_varlen", "idx_varlen_windows",
     "idx_topk_workspace_size", "idx_topk",
     "idx_prefill_rows_per_chunk", "idx_prefill_scratch_bytes",
-    "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_kv_cache_write",
+    "idx_prefill_schedule_ints", "idx_prefill_chunked_topk", "idx_prefill_chunked_topk_noalloc",
+    "idx_kv_cache_write",
     "idx_quantize_query", "idx_sparse_mla_workspace_size", "idx_sparse_mla_decode",
     "idx_validate_decode", "idx_status_string", "idx_last_error", "idx_version",
 )
@@ -104,6 +109,8 @@ def load(path: str = LIB_PATH):
         "idx_prefill_schedule_ints": (i64, [i32, i64, i64]),
         "idx_prefill_chunked_topk": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache), P, P,
                                           i32, i64, i64, i32, i32, P, i64, P, i64, P, P]),
+        "idx_prefill_chunked_topk_noalloc": (st, [ctypes.POINTER(Query), ctypes.POINTER(KVCache),
+                                                  P, P, i32, i64, i64, i32, i32, P, P]),
         "idx_kv_cache_write": (st, [P, i32, i64, i32, P, ctypes.POINTER(KVCache), P]),
         "idx_quantize_query": (st, [P, i32, i64, i32, P, ctypes.c_float,
                                     ctypes.POINTER(Query), P]),
@@ -236,6 +243,15 @@ def idx_prefill_chunked_topk(query: Query, kv: KVCache, block_table, visible_end
                                            ptr(cta_scratch), cta_scratch_ints, ptr(out_idx),
                                            stream_handle(stream)),
            "idx_prefill_chunked_topk")
+
+
+def idx_prefill_chunked_topk_noalloc(query: Query, kv: KVCache, block_table, visible_end, T, W,
+                                     budget_bytes, k, index_base, out_idx, stream=None):
+    _check(load().idx_prefill_chunked_topk_noalloc(ctypes.byref(query), ctypes.byref(kv),
+                                                   ptr(block_table), ptr(visible_end), T, W,
+                                                   budget_bytes, k, index_base, ptr(out_idx),
+                                                   stream_handle(stream)),
+           "idx_prefill_chunked_topk_noalloc")
 
 
 def idx_last_error_message() -> str:

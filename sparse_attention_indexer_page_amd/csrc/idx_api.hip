@@ -2,6 +2,7 @@
 // Every check here runs before any HIP call, so a rejected call leaves the
 // device untouched; nothing here allocates, frees or synchronizes.
 #include <cmath>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -130,6 +131,39 @@ int32_t prefill_ctas(int64_t chunk_rows) {
   int64_t segs = (chunk_rows + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg;
   if (segs < 1) segs = 1;
   return (int32_t)(segs < 1024 ? segs : 1024);
+}
+
+// Fixed device scratch of the no-allocation prefill entry: the chunk's fp32
+// logits, then the chunks' schedules. One copy per GPU the library runs on,
+// held until the process ends. In host code `g_noalloc_scratch` names a
+// host-side stand-in, not device memory: every host use goes through the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kNoAllocLogitsBytes = IDX_NOALLOC_LOGITS_BYTES;
+constexpr int64_t kNoAllocScheduleInts = IDX_NOALLOC_SCHEDULE_INTS;
+__device__ __align__(256) uint8_t g_noalloc_scratch[kNoAllocLogitsBytes + 4 * kNoAllocScheduleInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+uint8_t *g_noalloc_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+idx_status noalloc_scratch(uint8_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(IDX_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_noalloc_scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_noalloc_ptr[dev] = static_cast<uint8_t *>(p);
+  }
+  *out = g_noalloc_ptr[dev];
+  return IDX_OK;
 }
 
 } // namespace
@@ -536,12 +570,11 @@ int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes) {
   return chunks * idx_schedule_ints(prefill_ctas(rows)); // one schedule per chunk
 }
 
-idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
-                                    const int32_t *block_table, const int32_t *visible_end,
-                                    int32_t T, int64_t W, int64_t budget_bytes, int32_t k,
-                                    int32_t index_base, float *logits_scratch,
-                                    int64_t scratch_bytes, int32_t *cta_scratch,
-                                    int64_t cta_scratch_ints, int32_t *out_idx, void *stream) {
+static idx_status prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
+                                const int32_t *block_table, const int32_t *visible_end, int32_t T,
+                                int64_t W, int64_t budget_bytes, int32_t k, int32_t index_base,
+                                float *logits_scratch, int64_t scratch_bytes, int32_t *cta_scratch,
+                                int64_t cta_scratch_ints, int32_t *out_idx, void *stream) {
   idx_status st = check_query(q);
   if (st != IDX_OK) return st;
   if ((st = check_cache(kv, q->dtype)) != IDX_OK) return st;
@@ -620,6 +653,50 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
     if (e != hipSuccess) return hip_fail(e, "prefill top-k launch");
   }
   return ok();
+}
+
+
+idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
+                                    const int32_t *block_table, const int32_t *visible_end,
+                                    int32_t T, int64_t W, int64_t budget_bytes, int32_t k,
+                                    int32_t index_base, float *logits_scratch,
+                                    int64_t scratch_bytes, int32_t *cta_scratch,
+                                    int64_t cta_scratch_ints, int32_t *out_idx, void *stream) {
+  return prefill_chunked_topk(q, kv, block_table, visible_end, T, W, budget_bytes, k, index_base,
+                              logits_scratch, scratch_bytes, cta_scratch, cta_scratch_ints,
+                              out_idx, stream);
+}
+
+idx_status idx_prefill_chunked_topk_noalloc(const idx_query *q, const idx_kv_cache *kv,
+                                            const int32_t *block_table,
+                                            const int32_t *visible_end, int32_t T, int64_t W,
+                                            int64_t budget_bytes, int32_t k, int32_t index_base,
+                                            int32_t *out_idx, void *stream) {
+  // Size checks first, on the host, before any HIP call.
+  if (T < 1) return fail(IDX_ERR_INVALID, "T must be >= 1");
+  if (W < 1) return fail(IDX_ERR_INVALID, "W must be >= 1");
+  if (W > idx::kTopkMaxW)
+    return fail(IDX_ERR_UNSUPPORTED, "W = %lld above the %d-wide in-register top-k", (long long)W,
+                idx::kTopkMaxW);
+  if (budget_bytes < 1) return fail(IDX_ERR_INVALID, "budget_bytes must be >= 1");
+  // The fixed logits scratch is one more cap on the budget; the selection does
+  // not depend on the budget, so the result equals idx_prefill_chunked_topk's.
+  const int64_t budget = budget_bytes < kNoAllocLogitsBytes ? budget_bytes : kNoAllocLogitsBytes;
+  const int64_t need_logits = idx_prefill_scratch_bytes(T, W, budget);
+  const int64_t need_ints = idx_prefill_schedule_ints(T, W, budget);
+  if (need_logits > kNoAllocLogitsBytes || need_ints > kNoAllocScheduleInts)
+    return fail(IDX_ERR_WORKSPACE,
+                "T = %d, W = %lld need %lld B of logits and %lld schedule ints; the fixed scratch "
+                "holds %lld B and %lld ints",
+                T, (long long)W, (long long)need_logits, (long long)need_ints,
+                (long long)kNoAllocLogitsBytes, (long long)kNoAllocScheduleInts);
+  uint8_t *base = nullptr;
+  idx_status st = noalloc_scratch(&base);
+  if (st != IDX_OK) return st;
+  return prefill_chunked_topk(q, kv, block_table, visible_end, T, W, budget, k, index_base,
+                              reinterpret_cast<float *>(base), kNoAllocLogitsBytes,
+                              reinterpret_cast<int32_t *>(base + kNoAllocLogitsBytes),
+                              kNoAllocScheduleInts, out_idx, stream);
 }
 
 } // extern "C"

@@ -373,3 +373,28 @@ def test_topk_row_loads_stay_inside_the_row(wave_kernel, NT, buckets):
                     assert off + 4 <= 4 * E, (IPT, E, off)
                     seen[off // 4] += 1
             assert all(c == 1 for c in seen), (IPT, E)
+
+
+def test_prefill_noalloc_rejects_plans_beyond_its_fixed_scratch(lib):
+    """The no-allocation prefill checks on the host, before any HIP call, that
+    the chunk plan fits its fixed scratch: at W = 65536 the 64 MiB logits
+    cap allows 256 rows per chunk, and 300000 rows then need 1172 schedules
+    of 129 work groups, more than the 2^18 schedule entries it holds."""
+    q, kv = _q(), _kv()
+    fake = ctypes.c_void_p(0x10000)
+    st = lib.idx_prefill_chunked_topk_noalloc(ctypes.byref(q), ctypes.byref(kv), fake, fake,
+                                              300000, 65536, 1 << 40, 2048, 0, fake, None)
+    assert st == idx.IDX_ERR_WORKSPACE
+    assert b"fixed scratch" in lib.idx_last_error()
+    for T, W, status in ((0, 4096, idx.IDX_ERR_INVALID), (10, 0, idx.IDX_ERR_INVALID),
+                         (10, 65537, idx.IDX_ERR_UNSUPPORTED)):
+        assert lib.idx_prefill_chunked_topk_noalloc(ctypes.byref(q), ctypes.byref(kv), fake, fake,
+                                                    T, W, 1 << 30, 16, 0, fake, None) == status
+
+
+def test_noalloc_capacities_match_the_header():
+    text = open(HEADER).read()
+    logits = re.search(r"#define IDX_NOALLOC_LOGITS_BYTES \((\d+)ll << (\d+)\)", text)
+    ints = re.search(r"#define IDX_NOALLOC_SCHEDULE_INTS \((\d+)ll << (\d+)\)", text)
+    assert int(logits.group(1)) << int(logits.group(2)) == binding.IDX_NOALLOC_LOGITS_BYTES
+    assert int(ints.group(1)) << int(ints.group(2)) == binding.IDX_NOALLOC_SCHEDULE_INTS
