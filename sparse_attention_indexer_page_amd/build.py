@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libidx.so")
 # digest of the sources and flags the library at LIB was built from
 DIGEST = LIB + ".digest"
-SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "topk.hip", "kv_write.hip",
+SOURCES = ["idx_api.hip", "schedule.hip", "mqa_logits.hip", "prefill.hip", "topk.hip", "kv_write.hip",
            "q_quant.hip", "sparse_mla.hip", "validate.hip"]
 ARCH = "gfx950"
 

@@ -122,15 +122,13 @@ int64_t prefill_chunk_rows(int32_t T, int64_t W, int64_t budget) {
   return rows < 1 ? 1 : rows;
 }
 
-// Work groups of a prefill chunk: single waves, one per segment of query
-// rows, at most 1024 (four per CU of an MI355X, one per SIMD; each walks an
-// equal share of the chunk's key blocks). Measured on the chunked-prefill
-// workload: 1024 work groups 104.7 + 257.9 us per call's two chunks, 2048:
-// 106.7 + 262.5 us; one row per wave 108.6 + 268.0 us.
+// Work groups of a prefill chunk: one per block of query rows, at most 512
+// (two resident 8-wave groups per CU of an MI355X; each walks an equal share
+// of the chunk's key blocks).
 int32_t prefill_ctas(int64_t chunk_rows) {
   int64_t segs = (chunk_rows + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg;
   if (segs < 1) segs = 1;
-  return (int32_t)(segs < 1024 ? segs : 1024);
+  return (int32_t)(segs < 512 ? segs : 512);
 }
 
 // Fixed device scratch of the no-allocation prefill entry: the chunk's fp32

@@ -23,9 +23,9 @@ constexpr int32_t kMaxSegLen = 1 << 22;
 __host__ __device__ inline int32_t clamp_seg_len(int32_t v) {
   return v < 0 ? 0 : (v > kMaxSegLen ? kMaxSegLen : v);
 }
-constexpr int kPrefillRowsPerSeg = 2;  // query rows sharing one K stream (one wave) in prefill
-// Work-split cost of entering a segment, in key blocks: a prefill segment
-// reloads its query rows (about one block's scoring time); a decode
+constexpr int kPrefillRowsPerSeg = 7;  // query rows sharing one K stream in prefill
+// Work-split cost of entering a segment, in key blocks: a prefill row block
+// reloads seven query rows (about one block's scoring time); a decode
 // sequence's query load hides under the key stream.
 constexpr int kPrefillEntryCost = 1;
 constexpr int kDecodeEntryCost = 0;

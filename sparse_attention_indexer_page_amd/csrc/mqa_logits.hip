@@ -6,14 +6,6 @@
 // the "FP8 paged-MQA logits" kernel of vllm-project/DeepGEMM PR #14, which
 // name the op; the formula is the stated problem this library implements).
 //
-// One pipeline serves decode and prefill. A segment is a decode sequence
-// (its next_n query rows share one key stream) or, in prefill, a pair of
-// consecutive query rows of one sequence (ATOM PR #1709, commit on
-// right-sizing the prefill logits: rows see [0, visible_end) of a
-// right-sized width, in Q-row chunks); a prefill key block is read from L2
-// by every wave that scores it (the keys of a prefill chunk, a few hundred
-// KB, stay in L2; the loads keep the default cache policy).
-//
 // Design (one 64-lane wave per work group; the schedule hands each wave a
 // contiguous run of (segment, block) items):
 //   * A segment's query rows stay in VGPRs as MFMA A operands: row r, head
@@ -115,27 +107,9 @@ __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const
 // Returns the segment's length. With row offsets the count is clamped to
 // [0, next_n] and rows outside [0, row_cap) become padding, so malformed
 // offsets can only drop rows, never address outside the buffers.
-//
-// Prefill (PRE): segment s is the NROW consecutive query rows starting at
-// row0 + s * NROW of the chunk [row0, row_end); row r sees visible_end[r]
-// keys and writes logits row r - row0 (the chunk's scratch).
-template <int NROW, bool PRE>
+template <int NROW>
 __device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows, int32_t *E,
                                        int32_t *out_rows) {
-  if (PRE) {
-    int32_t L = 0;
-#pragma unroll
-    for (int i = 0; i < NROW; ++i) {
-      const int r = a.row0 + s * NROW + i;
-      const bool live = r < a.row_end;
-      const int32_t e = live ? clamp_seg_len(uniform_load(a.lens + r)) : 0;
-      rows[i] = live ? r : -1;
-      E[i] = e;
-      out_rows[i] = live ? r - a.row0 : -1;
-      L = e > L ? e : L;
-    }
-    return L;
-  }
   const int32_t len = uniform_load(a.lens + s);
   int32_t base = s * a.next_n, n = a.next_n;
   if (a.row_offsets != nullptr) {
@@ -158,20 +132,8 @@ __device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows
   return L;
 }
 
-// Length of segment s, clamped as the work split counts it: decode, the
-// sequence's length (its last row's visible length); prefill, the largest
-// visible end of its rows.
-template <int NROW, bool PRE> __device__ inline int32_t segment_length(const LogitsArgs &a, int s) {
-  if (PRE) {
-    int32_t L = 0;
-#pragma unroll
-    for (int i = 0; i < NROW; ++i) {
-      const int r = a.row0 + s * NROW + i;
-      const int32_t e = r < a.row_end ? uniform_load(a.lens + r) : 0;
-      L = e > L ? e : L;
-    }
-    return clamp_seg_len(L);
-  }
+// Length of sequence s (its last row's visible length).
+__device__ inline int32_t segment_length(const LogitsArgs &a, int s) {
   return clamp_seg_len(uniform_load(a.lens + s));
 }
 
@@ -187,19 +149,19 @@ __device__ inline bool in_range(const LogitsArgs &a, const Walk &w) {
 }
 
 // Moves to the first block of the next segment that has blocks.
-template <int NROW, bool PRE> __device__ inline bool next_segment(const LogitsArgs &a, Walk &w) {
+__device__ inline bool next_segment(const LogitsArgs &a, Walk &w) {
   w.blk = 0;
   while (true) {
     ++w.s;
     if (!in_range(a, w)) return false;
-    w.nb = (segment_length<NROW, PRE>(a, w.s) + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
+    w.nb = (segment_length(a, w.s) + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
     if (w.nb > 0) return true;
   }
 }
 
-template <int NROW, bool PRE> __device__ inline bool advance(const LogitsArgs &a, Walk &w) {
+__device__ inline bool advance(const LogitsArgs &a, Walk &w) {
   if (++w.blk < w.nb) return in_range(a, w);
-  return next_segment<NROW, PRE>(a, w);
+  return next_segment(a, w);
 }
 
 // Inclusive prefix sum over the wave's lanes with DPP moves (no LDS round
@@ -290,20 +252,19 @@ template <int TPB> struct KBlock {
   int t0;           // first token of the block
 };
 
-// Decode reads key bytes and key scales once per launch: the loads carry the
+// Key bytes and key scales are read once per launch: the loads carry the
 // non-temporal hint (cache policy nt), so the stream does not displace the
 // small data every launch reuses (lengths, block tables, queries, weights)
 // or the logits the top-k reads next (decode scoring 35.6 -> 33.4 us on the
-// batched-decode workload, measured). Prefill reads the same keys for every
-// row of the chunk, so its loads keep the default policy (the keys stay in L2).
-template <bool PRE> constexpr int key_cache_policy() { return PRE ? 0 : 2; } // aux bits: nt
+// batched-decode workload, measured).
+constexpr int kStream = 2; // buffer-load aux bits: nt
 
-template <bool PRE> __device__ inline v4i load16_key(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, key_cache_policy<PRE>());
+__device__ inline v4i load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
 }
 
-template <bool PRE> __device__ inline uint32_t load4_key(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, key_cache_policy<PRE>());
+__device__ inline uint32_t load4_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStream);
 }
 
 // Physical page of logical page lp of sequence s, or -1 past the table row.
@@ -322,7 +283,7 @@ __device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp) {
 // compiler's wait counts partial (a path without them would force it to wait
 // for every load, including the next block's, before the first MFMA).
 // The block's page comes from the caller (pg < 0: nothing to load).
-template <int DT, int TPB, bool PRE>
+template <int DT, int TPB>
 __device__ inline void issue_block_page(const LogitsArgs &a, int blk, int64_t pg,
                                         KBlock<TPB> &kb) {
   const int lane = threadIdx.x & 63;
@@ -344,26 +305,26 @@ __device__ inline void issue_block_page(const LogitsArgs &a, int blk, int64_t pg
     // one scale per lane: the token this lane holds after the head-sum
     // reduction (t0 + lane for 4-tile blocks, t0 + 16*(g/2) + col for 2-tile)
     const uint32_t slot = (uint32_t)(slot0 + (TPB == 4 ? lane : 16 * (g >> 1) + col));
-    kb.ksr = load4_key<PRE>(sr, slot * (uint32_t)a.scale_row_stride);
+    kb.ksr = load4_stream(sr, slot * (uint32_t)a.scale_row_stride);
   }
 #pragma unroll
   for (int ti = 0; ti < TPB; ++ti) {
     const uint32_t slot = (uint32_t)(slot0 + ti * kTile + col);
     const uint32_t off = slot * (uint32_t)a.row_stride;
     if (DT == IDX_FP8_E4M3) {
-      kb.kb[ti] = cat(load16_key<PRE>(kr, off + 16 * g), load16_key<PRE>(kr, off + 64 + 16 * g));
+      kb.kb[ti] = cat(load16_stream(kr, off + 16 * g), load16_stream(kr, off + 64 + 16 * g));
     } else {
-      const v4i lo = load16_key<PRE>(kr, off + 16 * g);
+      const v4i lo = load16_stream(kr, off + 16 * g);
       kb.kb[ti] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-      kb.ks[ti] = load4_key<PRE>(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
+      kb.ks[ti] = load4_stream(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
     }
   }
 }
 
-template <int DT, int TPB, bool PRE>
+template <int DT, int TPB>
 __device__ inline void issue_block(const LogitsArgs &a, const Walk &w, bool live, KBlock<TPB> &kb) {
   const int lp = (w.blk * a.block_tokens) / a.page_size;
-  issue_block_page<DT, TPB, PRE>(a, w.blk, live ? page_of(a, w.s, lp) : -1, kb);
+  issue_block_page<DT, TPB>(a, w.blk, live ? page_of(a, w.s, lp) : -1, kb);
 }
 
 // MFMAs of one 16-token tile against every head tile of every row.
@@ -466,23 +427,23 @@ __device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q
   }
 }
 
-template <int DT, int NROW, bool PRE>
+template <int DT, int NROW>
 __device__ inline int32_t enter_segment(const LogitsArgs &a, int s, QRegs<DT, NROW> &Q) {
   int32_t rows[NROW], E[NROW], orow[NROW];
-  const int32_t L = segment_rows<NROW, PRE>(a, s, rows, E, orow);
+  const int32_t L = segment_rows<NROW>(a, s, rows, E, orow);
   load_query<DT, NROW>(Q, a, rows, E, orow);
   return L;
 }
 
 // One pipeline step: `cur` holds the loaded current block; the next block's
 // loads go into `nxt` before `cur` is scored. Returns false at the end.
-template <int DT, int NROW, int TPB, bool PRE>
+template <int DT, int NROW, int TPB>
 __device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, QRegs<DT, NROW> &Q,
                                      int32_t &L, KBlock<TPB> &cur, KBlock<TPB> &nxt,
                                      OutStage<NROW> &st, StageState &ss) {
   Walk wn = w;
-  const bool more = advance<NROW, PRE>(a, wn);
-  issue_block<DT, TPB, PRE>(a, wn, more, nxt);
+  const bool more = advance(a, wn);
+  issue_block<DT, TPB>(a, wn, more, nxt);
   if (ss.base < 0) {
     ss.base = cur.t0 & ~(kStageTokens - 1);
     ss.lo = cur.t0;
@@ -494,17 +455,17 @@ __device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, QRegs<DT, NRO
   if (!more || wn.s != w.s || ((wn.blk * a.block_tokens) & ~(kStageTokens - 1)) != ss.base)
     flush_stage<DT, NROW>(a, Q, st, ss);
   if (!more) return false;
-  if (wn.s != w.s) L = enter_segment<DT, NROW, PRE>(a, wn.s, Q);
+  if (wn.s != w.s) L = enter_segment<DT, NROW>(a, wn.s, Q);
   w = wn;
   return true;
 }
 
-// The scores of one work group's range of (segment, block) items.
-template <int DT, int NROW, int TPB, bool PRE> __device__ inline void score_range(const LogitsArgs &a) {
+template <int DT, int NROW, int TPB>
+__global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   const int c = blockIdx.x;
   Walk w;
   int32_t len0;
-  if (PRE || a.cta_info != nullptr) {
+  if (a.cta_info != nullptr) {
     w.s = uniform_load(a.cta_info + 2 * c);
     w.blk = uniform_load(a.cta_info + 2 * c + 1);
     w.s = w.s > 0 ? w.s : 0; // a buffer never written by the builder must not index backwards
@@ -512,7 +473,7 @@ template <int DT, int NROW, int TPB, bool PRE> __device__ inline void score_rang
     w.se = uniform_load(a.cta_info + 2 * c + 2);
     w.be = uniform_load(a.cta_info + 2 * c + 3);
     if (!in_range(a, w)) return;
-    len0 = segment_length<NROW, PRE>(a, w.s);
+    len0 = segment_length(a, w.s);
   } else {
     len0 = own_range(a, c, w);
     if (!in_range(a, w)) return;
@@ -525,30 +486,18 @@ template <int DT, int NROW, int TPB, bool PRE> __device__ inline void score_rang
   w.nb = (len0 + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
   KBlock<TPB> A, B;
   if (w.blk < w.nb) {
-    issue_block_page<DT, TPB, PRE>(a, w.blk, pg0, A);
+    issue_block_page<DT, TPB>(a, w.blk, pg0, A);
   } else { // empty or stale entry
-    if (!next_segment<NROW, PRE>(a, w)) return;
-    issue_block<DT, TPB, PRE>(a, w, true, A);
+    if (!next_segment(a, w)) return;
+    issue_block<DT, TPB>(a, w, true, A);
   }
   QRegs<DT, NROW> Q;
-  int32_t L = enter_segment<DT, NROW, PRE>(a, w.s, Q);
+  int32_t L = enter_segment<DT, NROW>(a, w.s, Q);
   __shared__ OutStage<NROW> st;
   StageState ss;
-  while (pipeline_step<DT, NROW, TPB, PRE>(a, w, Q, L, A, B, st, ss) &&
-         pipeline_step<DT, NROW, TPB, PRE>(a, w, Q, L, B, A, st, ss)) {
+  while (pipeline_step<DT, NROW, TPB>(a, w, Q, L, A, B, st, ss) &&
+         pipeline_step<DT, NROW, TPB>(a, w, Q, L, B, A, st, ss)) {
   }
-}
-
-template <int DT, int NROW, int TPB>
-__global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
-  score_range<DT, NROW, TPB, false>(a);
-}
-
-// Prefill: the same single-wave pipeline over segments of kPrefillRowsPerSeg
-// consecutive query rows of one sequence, from a schedule buffer.
-template <int DT, int TPB>
-__global__ __launch_bounds__(64) void prefill_logits_kernel(LogitsArgs a) {
-  score_range<DT, kPrefillRowsPerSeg, TPB, true>(a);
 }
 
 template <int DT, int NROW, int TPB> hipError_t launch_tpb(const LogitsArgs &a, hipStream_t s) {
@@ -561,17 +510,6 @@ template <int DT, int NROW> hipError_t launch(const LogitsArgs &a, hipStream_t s
   if (a.block_tokens == 32) return launch_tpb<DT, NROW, 2>(a, s);
   if (a.block_tokens == 64) return launch_tpb<DT, NROW, 4>(a, s);
   return hipErrorInvalidValue;
-}
-
-template <int DT> hipError_t launch_prefill(const LogitsArgs &a, hipStream_t s) {
-  if (a.cta_info == nullptr) return hipErrorInvalidValue;
-  if (a.block_tokens == 32)
-    hipLaunchKernelGGL((prefill_logits_kernel<DT, 2>), dim3(a.n_ctas), dim3(64), 0, s, a);
-  else if (a.block_tokens == 64)
-    hipLaunchKernelGGL((prefill_logits_kernel<DT, 4>), dim3(a.n_ctas), dim3(64), 0, s, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 template <int DT> hipError_t launch_decode(const LogitsArgs &a, hipStream_t s) {
@@ -591,12 +529,6 @@ hipError_t launch_logits_fp8_decode(const LogitsArgs &a, hipStream_t s) {
 }
 hipError_t launch_logits_mxfp4_decode(const LogitsArgs &a, hipStream_t s) {
   return launch_decode<IDX_MXFP4>(a, s);
-}
-hipError_t launch_logits_fp8_prefill(const LogitsArgs &a, hipStream_t s) {
-  return launch_prefill<IDX_FP8_E4M3>(a, s);
-}
-hipError_t launch_logits_mxfp4_prefill(const LogitsArgs &a, hipStream_t s) {
-  return launch_prefill<IDX_MXFP4>(a, s);
 }
 
 } // namespace idx
