@@ -347,7 +347,7 @@ FP8_MFMA_FLOPS = 16 * 16 * 128 * 2  # one v_mfma_f32_16x16x128_f8f6f4
 
 def prefill_source_digest():
     h = hashlib.sha256()
-    for f in ("mqa_logits.hip", "device_common.h", "internal.h"):
+    for f in ("prefill.hip", "device_common.h", "internal.h"):
         with open(os.path.join(ROOT, "sparse_attention_indexer_page_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -672,6 +672,113 @@ def cpu_baseline(case, budget_s):
     }
 
 
+CEILINGS_MD = os.path.join(ROOT, "profiles", "ceilings_mi355x.md")
+
+
+def ceilings(torch, write_dir=None):
+    """Roofline ceilings measured on this GPU with the kernels of
+    sparse_attention_indexer_page_amd/ceilings: the paged streaming-read rate
+    (random key pages, the scoring kernel's MFMA-ordered loads and linear 1 KB
+    loads) and the FP8 MFMA rate alone, with the scoring epilogue, and the
+    epilogue alone. Writes profiles/ceilings_mi355x.md."""
+    import ctypes
+    import numpy as np
+    from sparse_attention_indexer_page_amd import build
+    if not os.path.exists(build.CEILINGS_LIB):
+        build.build_ceilings()
+    lib = ctypes.CDLL(build.CEILINGS_LIB)
+    P = ctypes.c_void_p
+    lib.ceil_stream_pages.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    lib.ceil_mfma_epilogue.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, reps=4):
+        best = 1e30
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise SystemExit("ceiling kernel launch failed: %d" % rc)
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return best
+
+    res = {"stream": [], "mfma": []}
+    pool_bytes = 2 << 30  # 8x the 256 MiB last-level cache; each page read once
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    out = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(7)
+    for kind, (rows, stride) in ((0, (32, 144)), (1, (64, 128))):
+        page = rows * stride
+        n_pages = pool_bytes // page // 4  # 512 MiB of pages touched per pass
+        for waves in (1024, 2048):
+            ppw = (n_pages // waves) // 2 * 2
+            pages = torch.from_numpy(rng.permutation(n_pages)[:waves * ppw].astype(np.int32)).cuda()
+            for linear in (0, 1):
+                t = timed(lambda: lib.ceil_stream_pages(pool.data_ptr(), pages.data_ptr(), ppw, waves,
+                                                        kind, linear, out.data_ptr(), stream))
+                gbs = waves * ppw * page / t / 1e9
+                res["stream"].append({"page": "%d x %d B" % (rows, stride), "waves": waves,
+                                      "loads": "linear 1 KB" if linear else "MFMA order (16 rows x 64 B)",
+                                      "us": t * 1e6, "gbs": gbs, "frac_of_8tbs": gbs / HBM_PEAK_GBS})
+                log("ceiling stream %s, %d waves, %s: %.0f GB/s" % (
+                    res["stream"][-1]["page"], waves, res["stream"][-1]["loads"], gbs))
+    del pool
+    # FP8 operands: a low-entropy pattern, and random finite E4M3 codes (what
+    # quantized keys and queries look like; they draw more power and the
+    # clock drops, so this is the ceiling the scoring kernels face)
+    low = (np.arange(1024, dtype=np.int64) * 2654435761 & 0x3C3C3C3C).astype(np.int32)
+    codes = rng.integers(0, 256, size=4096, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] -= 1  # no NaN codes
+    operands = (("low-entropy pattern", low), ("random FP8 codes", codes.view(np.int32)))
+    fout = torch.empty(256 * 1024, dtype=torch.float32, device="cuda")
+    iters = 4000
+    for (data, host), threads in [(o, t) for o in operands for t in (256, 512, 1024)]:
+        inp = torch.from_numpy(np.ascontiguousarray(host)).cuda()
+        row = {"operands": data, "waves_per_simd": threads // 256}
+        for mode, name in ((0, "mfma"), (1, "epilogue"), (2, "mfma_and_epilogue")):
+            t = timed(lambda: lib.ceil_mfma_epilogue(inp.data_ptr(), fout.data_ptr(), iters, mode, 256,
+                                                     threads, stream), reps=3)
+            waves = 256 * threads // 64
+            row[name + "_us"] = t * 1e6
+            if mode != 1:  # 8 MFMAs of 65536 flops per wave per iteration
+                row[name + "_tflops"] = waves * iters * 8 * 65536 / t / 1e12
+            else:          # 32 scores (2*relu + multiply-add) per lane per iteration
+                row["epilogue_gscores_per_s"] = waves * 64 * iters * 32 / t / 1e9
+        row["mfma_and_epilogue_frac_of_5pf"] = row["mfma_and_epilogue_tflops"] / FP8_MFMA_PEAK_TFLOPS
+        row["mfma_frac_of_5pf"] = row["mfma_tflops"] / FP8_MFMA_PEAK_TFLOPS
+        res["mfma"].append(row)
+        log("ceiling MFMA, %s, %d waves/SIMD: MFMA alone %.0f TF, with the epilogue %.0f TF (%.1f%% of 5 PF)" % (
+            data, row["waves_per_simd"], row["mfma_tflops"], row["mfma_and_epilogue_tflops"],
+            100 * row["mfma_and_epilogue_frac_of_5pf"]))
+    cmd = "python3 bench.py --ceilings"
+    lines = ["# Roofline ceilings measured on the MI355X", "", "Command (repository root, one MI355X):", "",
+             "```", cmd, "```", "",
+             "Kernels: `sparse_attention_indexer_page_amd/ceilings/ceilings.hip`.", "",
+             "## Paged streaming read (random pages, each read once, 512 MiB per pass, one page ahead per wave)",
+             "", "| page | waves | loads | us | GB/s | of 8 TB/s |", "|---|---|---|---|---|---|"]
+    for r in res["stream"]:
+        lines.append("| %s | %d | %s | %.1f | %.0f | %.1f%% |" % (r["page"], r["waves"], r["loads"], r["us"],
+                                                               r["gbs"], 100 * r["frac_of_8tbs"]))
+    lines += ["", "## FP8 MFMA (16x16x128) and the scoring epilogue (256 work groups)", "",
+              "Per wave and iteration: 8 MFMAs (mfma), the epilogue of 32 scores per lane: s + |s| and a "
+              "multiply-add each (epilogue), or both in the scoring kernel's proportion (8 VALU ops per MFMA).",
+              "", "| operands | waves/SIMD | MFMA alone TF/s | epilogue alone G scores/s | both: TF/s | both: of 5 PF |",
+              "|---|---|---|---|---|---|"]
+    for r in res["mfma"]:
+        lines.append("| %s | %d | %.0f | %.0f | %.0f | %.1f%% |" % (
+            r["operands"], r["waves_per_simd"], r["mfma_tflops"], r["epilogue_gscores_per_s"], r["mfma_and_epilogue_tflops"],
+            100 * r["mfma_and_epilogue_frac_of_5pf"]))
+    out_md = os.path.join(write_dir, os.path.basename(CEILINGS_MD)) if write_dir else CEILINGS_MD
+    os.makedirs(os.path.dirname(out_md), exist_ok=True)
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log("wrote " + out_md)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -694,7 +801,11 @@ def main():
     ap.add_argument("--sparse-attention-only", action="store_true",
                     help="time only the sparse attention over the selection (one JSON line)")
     ap.add_argument("--all-workloads", action="store_true",
-                    help="also time the other decode workloads (single sequence, MTP page 32, MXFP4)")
+                    help="(the default run times every decode workload; kept for the profile commands)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the streaming-read and MFMA ceilings (writes profiles/ceilings_mi355x.md)")
+    ap.add_argument("--write-dir", default=None,
+                    help="write generated summaries here instead of profiles/")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write the profiles/ kernel-trace summary of a --kernel-trace --stats run")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -762,6 +873,9 @@ def main():
     idx.load()
     torch.cuda.set_device(0)
 
+    if args.ceilings:
+        ceilings(torch, args.write_dir)
+        return
     if args.counters:
         counter_run(args, torch, idx, synth)
         return
@@ -799,7 +913,7 @@ def main():
         log("sparse attention: %.1f us per call, %.0f GB/s, %.1f TFLOP/s bf16" % (
             mla["us_per_call"], mla["achieved_gbs"], mla["bf16_tflops"]))
     others = []
-    if args.all_workloads:
+    if not args.no_prefill:
         for wl in (1, 3, 5):
             o = decode_bench(args, torch, idx, synth, wl)
             log("workload %d: step %.3f ms, scoring kernel %.3f ms avg, %.0f GB/s (%.1f%% of peak)" % (
@@ -808,8 +922,10 @@ def main():
             others.append({"workload": synth.WORKLOADS[wl], "tokens": o["tokens"],
                            "ms_per_step": o["step_ms"], "scoring_kernel_us": o["kern_avg_ms"] * 1e3,
                            "tokens_per_s": o["tokens"] / (o["step_ms"] * 1e-3),
+                           "algorithmic_bytes_per_launch": o["launch_bytes"],
                            "achieved_gbs": o["achieved_gbs"],
-                           "hbm_frac": o["achieved_gbs"] / HBM_PEAK_GBS})
+                           "hbm_frac": o["achieved_gbs"] / HBM_PEAK_GBS,
+                           "n_ctas": o["n_ctas"]})
     cpu = None if args.no_cpu_baseline else cpu_baseline(d["case"], args.cpu_budget_s)
 
     value = d["tokens"] / (d["step_ms"] * 1e-3)

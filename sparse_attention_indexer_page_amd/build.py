@@ -107,5 +107,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CEILINGS_SRC = os.path.join(HERE, "ceilings", "ceilings.hip")
+CEILINGS_LIB = os.path.join(HERE, "ceilings", "libidx_ceilings.so")
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """Compile the roofline-ceiling measurement kernels (bench.py --ceilings)
+    into their own library; they are not part of libidx.so."""
+    tmp = CEILINGS_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared"] + _flags() + ["-o", tmp, CEILINGS_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("compiling %s failed:\n%s%s" % (CEILINGS_SRC, res.stdout, res.stderr))
+    os.replace(tmp, CEILINGS_LIB)
+    return CEILINGS_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_ceilings(verbose="-v" in sys.argv))
