@@ -53,9 +53,24 @@ template <int DT, int NROW> struct QRegs {
   int32_t out_row[NROW]; // logits row, or -1 for a padding row
 };
 
+// The weights times the rows' FP8 q scales (the scores' per-row factor).
 template <int DT, int NROW>
+__device__ inline void scale_weights(QRegs<DT, NROW> &Q, const float (&qs)[NROW]) {
+#pragma unroll
+  for (int i = 0; i < NROW; ++i)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Q.w[i][m][j] *= qs[i];
+}
+
+// Issues the loads of a segment's query rows: A operands, weights and (FP8)
+// the per-row q scales, returned in qs. With WAIT the loads are waited for
+// and the weights scaled here; without, the caller does both, so no loaded
+// value is consumed before its other loads have gone out.
+template <int DT, int NROW, bool WAIT = true>
 __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const int32_t *rows,
-                                  const int32_t *E, const int32_t *out_rows) {
+                                  const int32_t *E, const int32_t *out_rows, float (&qs)[NROW]) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int hl = lane & 15;
@@ -72,11 +87,12 @@ __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const
 #pragma unroll
         for (int j = 0; j < 4; ++j) Q.w[i][m][j] = 0.f;
       }
+      qs[i] = 1.f;
       continue;
     }
-    float qs = 1.f;
+    qs[i] = 1.f;
     if (DT == IDX_FP8_E4M3 && a.q_scale != nullptr)
-      qs = uniform_load(reinterpret_cast<const float *>(a.q_scale) + r);
+      qs[i] = uniform_load(reinterpret_cast<const float *>(a.q_scale) + r);
     const float *wrow = a.weights + (int64_t)r * kHeads;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -92,25 +108,29 @@ __device__ inline void load_query(QRegs<DT, NROW> &Q, const LogitsArgs &a, const
       }
       const v4f wv = *reinterpret_cast<const v4f *>(wrow + 16 * m + 4 * g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Q.w[i][m][j] = wv[j] * qs;
+      for (int j = 0; j < 4; ++j) Q.w[i][m][j] = wv[j]; // times qs once loaded
     }
   }
   // Wait for the query loads here, once per segment: left outstanding, the
   // compiler's wait for them at their first use would be a full vmcnt(0) in
   // every pass of the block loop, i.e. a wait for the next block's K loads.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // (The first segment's caller waits itself, after the first block's loads,
+  // and then scales the weights: nothing here may consume a loaded value.)
+  if (WAIT) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    scale_weights(Q, qs);
+  }
 }
 
-// Rows, visible lengths and output rows of sequence s: its n query rows
-// (next_n, or off[s+1] - off[s] with row offsets), row j seeing the first
-// len - (n - 1 - j) keys; the remaining register rows are padding (-1).
-// Returns the segment's length. With row offsets the count is clamped to
-// [0, next_n] and rows outside [0, row_cap) become padding, so malformed
-// offsets can only drop rows, never address outside the buffers.
+// Rows, visible lengths and output rows of sequence s of length len (as
+// stored, not clamped): its n query rows (next_n, or off[s+1] - off[s] with row offsets), row
+// j seeing the first len - (n - 1 - j) keys; the remaining register rows are
+// padding (-1). Returns the segment's length. With row offsets the count is
+// clamped to [0, next_n] and rows outside [0, row_cap) become padding, so
+// malformed offsets can only drop rows, never address outside the buffers.
 template <int NROW>
-__device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t *rows, int32_t *E,
-                                       int32_t *out_rows) {
-  const int32_t len = uniform_load(a.lens + s);
+__device__ inline int32_t segment_rows(const LogitsArgs &a, int s, int32_t len, int32_t *rows,
+                                       int32_t *E, int32_t *out_rows) {
   int32_t base = s * a.next_n, n = a.next_n;
   if (a.row_offsets != nullptr) {
     base = uniform_load(a.row_offsets + s);
@@ -430,8 +450,9 @@ __device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q
 template <int DT, int NROW>
 __device__ inline int32_t enter_segment(const LogitsArgs &a, int s, QRegs<DT, NROW> &Q) {
   int32_t rows[NROW], E[NROW], orow[NROW];
-  const int32_t L = segment_rows<NROW>(a, s, rows, E, orow);
-  load_query<DT, NROW>(Q, a, rows, E, orow);
+  float qs[NROW];
+  const int32_t L = segment_rows<NROW>(a, s, uniform_load(a.lens + s), rows, E, orow);
+  load_query<DT, NROW>(Q, a, rows, E, orow, qs);
   return L;
 }
 
@@ -478,21 +499,32 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
     len0 = own_range(a, c, w);
     if (!in_range(a, w)) return;
   }
-  // The first block's page is read together with the segment's length (the
-  // table entry exists whether or not the block does), so the first K loads
-  // wait for one round trip less; they go out before the query's, so those
-  // two latencies overlap as well.
+  // The first block's page is read together with the segment's stored
+  // length (the table entry exists whether or not the block does). The first
+  // segment's queries go out before either returns: their addresses need only
+  // the segment, so the query loads, the page lookup and then the first
+  // block's K loads overlap, with one wait for all of them.
   const int64_t pg0 = page_of(a, w.s, (w.blk * a.block_tokens) / a.page_size);
+  int32_t raw0 = uniform_load(a.lens + w.s);
   w.nb = (len0 + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
-  KBlock<TPB> A, B;
-  if (w.blk < w.nb) {
-    issue_block_page<DT, TPB>(a, w.blk, pg0, A);
-  } else { // empty or stale entry
+  const bool stale = w.blk >= w.nb; // empty or stale entry
+  if (stale) {
     if (!next_segment(a, w)) return;
-    issue_block<DT, TPB>(a, w, true, A);
+    raw0 = uniform_load(a.lens + w.s);
   }
   QRegs<DT, NROW> Q;
-  int32_t L = enter_segment<DT, NROW>(a, w.s, Q);
+  float qs[NROW];
+  int32_t L;
+  {
+    int32_t rows[NROW], E[NROW], orow[NROW];
+    L = segment_rows<NROW>(a, w.s, raw0, rows, E, orow);
+    load_query<DT, NROW, false>(Q, a, rows, E, orow, qs);
+  }
+  KBlock<TPB> A, B;
+  if (!stale) issue_block_page<DT, TPB>(a, w.blk, pg0, A);
+  else issue_block<DT, TPB>(a, w, true, A);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); // the queries and the first block
+  scale_weights(Q, qs);
   __shared__ OutStage<NROW> st;
   StageState ss;
   while (pipeline_step<DT, NROW, TPB>(a, w, Q, L, A, B, st, ss) &&
