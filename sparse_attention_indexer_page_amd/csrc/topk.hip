@@ -144,8 +144,9 @@ constexpr int kRankCap = 64; // candidates ranked directly by one wave
 struct TopkShared {
   uint32_t hist[kBins];
   uint32_t cand[kCandCap];
+  uint32_t cidx[kCandCap]; // row index of cand[i] when the candidates are a sampled threshold's
   uint32_t small[kRankCap];
-  uint32_t red[2 * 16];
+  uint32_t red[3 * 16];
   uint32_t sel[3]; // bin, count above it, count in it
   uint32_t ncand;
   uint32_t nsmall;
@@ -202,9 +203,11 @@ __device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit
   inbin = (int)sm.sel[2];
 }
 
-// Block-wide max and min of per-thread values (uniform result).
+// Block-wide max and min of per-thread values and sum of per-wave counts
+// (wave-uniform `cnt`); uniform results.
 template <int NT>
-__device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint32_t &mn) {
+__device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint32_t &mn,
+                                              uint32_t &cnt) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -214,14 +217,86 @@ __device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint
   if (lane == 0) {
     sm.red[wave] = mx;
     sm.red[16 + wave] = mn;
+    sm.red[32 + wave] = cnt;
   }
   __syncthreads();
   mx = 0u;
   mn = 0xFFFFFFFFu;
+  cnt = 0u;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     mx = sm.red[w] > mx ? sm.red[w] : mx;
     mn = sm.red[16 + w] < mn ? sm.red[16 + w] : mn;
+    cnt += sm.red[32 + w];
+  }
+}
+
+// Writes the selection in index order, given the rule found: every key >
+// thr, and of the keys == thr the first need_eq (all of them when all_ties;
+// then the rule is key >= thr_ge). Each wave owns N consecutive runs of 64
+// items; item q of this lane has key key_at(q) (0: nothing) and row index
+// idx_at(q), increasing with the wave, q and the lane. A counting pass gives
+// each wave its output offset, a writing pass places the indices with
+// ballots, so no sort is needed and ties go to the lower index.
+template <int NT, int N, typename KeyAt, typename IdxAt>
+__device__ __forceinline__ void emit_selection(TopkShared &sm, KeyAt key_at, IdxAt idx_at,
+                                               uint32_t thr, int need_eq, bool all_ties,
+                                               uint32_t thr_ge, int k, int32_t *out) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // ---- counting pass: per wave, keys taken wholesale and keys == thr
+  uint32_t n_gt = 0, n_eq = 0;
+  if (all_ties) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) n_gt += __popcll(__ballot(key_at(i) >= thr_ge));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) { // key 0 (no item) never reaches thr
+      const uint32_t x = key_at(i);
+      n_gt += __popcll(__ballot(x > thr));
+      n_eq += __popcll(__ballot(x == thr));
+    }
+  }
+  __syncthreads(); // every thread is done reading red and sel
+  if (lane == 0) {
+    sm.red[wave] = n_gt;
+    sm.red[16 + wave] = n_eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    gt_before += w < wave ? (int)sm.red[w] : 0;
+    eq_before += w < wave ? (int)sm.red[16 + w] : 0;
+  }
+
+  // ---- writing pass in index order
+  if (all_ties) {
+    int pos = gt_before;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool sel = key_at(i) >= thr_ge;
+      const uint64_t msel = __ballot(sel);
+      const int p = pos + lanes_below(msel);
+      if (sel && p < k) out[p] = idx_at(i);
+      pos += (int)__popcll(msel);
+    }
+  } else {
+    int pos = gt_before + (eq_before < need_eq ? eq_before : need_eq);
+    int eq_seen = eq_before;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t x = key_at(i);
+      const bool eq = x == thr;
+      const uint64_t meq = __ballot(eq);
+      const bool sel = x > thr || (eq && eq_seen + lanes_below(meq) < need_eq);
+      const uint64_t msel = __ballot(sel);
+      const int p = pos + lanes_below(msel);
+      if (sel && p < k) out[p] = idx_at(i);
+      pos += (int)__popcll(msel);
+      eq_seen += (int)__popcll(meq);
+    }
   }
 }
 
@@ -263,7 +338,14 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
       kmin = key[i] < kmin ? key[i] : kmin;
     }
   }
-  block_max_min<NT>(sm, kmax, kmin);
+  // One sampled key per thread, spread over the wave's run of the row (item
+  // lane % rounds of each lane), for the threshold estimate below.
+  const int si = lane % rounds;
+  uint32_t smp = 0u;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) smp = i == si ? key[i] : smp;
+  uint32_t n_smp = (uint32_t)__popcll(__ballot(smp != 0u));
+  block_max_min<NT>(sm, kmax, kmin, n_smp);
 
   // The candidates are the keys in [lo, hi]; `need` of them remain to take.
   uint32_t lo = kmin, hi = kmax;
@@ -272,20 +354,76 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   int need_eq = 0; // 0: every key >= thr + 1 is taken
   int n_eq_total = -1;
   bool done = false;
-  bool in_lds = false; // the candidates are sm.cand[0, nc)
+  bool in_lds = false;    // the candidates are sm.cand[0, nc)
+  bool compacted = false; // ... and they are every key >= lo, in index order (sm.cidx)
   int nc = 0;
 
-  // ---- pass 1 by value, linear between the row's extremes (a monotone map:
-  // a higher bin holds only larger scores; halved so nothing overflows)
+  // Bins by value, linear between the row's extremes (a monotone map: a
+  // higher bin holds only larger scores; halved so nothing overflows).
   const float h0 = key_float(kmin) * 0.5f;
   const float hr = key_float(kmax) * 0.5f - h0;
   const float scale = (float)kBins / hr;
-  if (hr > 0.f && scale < 3.0e38f) {
-    // one explicit FMA, so every evaluation of a key's bin rounds alike
-    auto vbin = [&](uint32_t kk) -> uint32_t {
-      const float x = __builtin_fmaf(key_float(kk), 0.5f, -h0) * scale;
-      return (uint32_t)fminf(x, (float)(kBins - 1));
-    };
+  const bool linear = hr > 0.f && scale < 3.0e38f;
+  // one explicit FMA, so every evaluation of a key's bin rounds alike
+  auto vbin = [&](uint32_t kk) -> uint32_t {
+    const float x = __builtin_fmaf(key_float(kk), 0.5f, -h0) * scale;
+    return (uint32_t)fminf(x, (float)(kBins - 1));
+  };
+
+  // ---- sampled threshold: the lower edge thr0 of the value bin that holds
+  // the m-th largest of the n_smp sampled keys, m chosen so that about
+  // min(2k, (k + kCandCap) / 2) of the row's keys lie at or above it. When
+  // between k and kCandCap of them do (counted exactly), those keys and their
+  // indices are compacted into LDS in index order, and the exact selection
+  // and the output run over them alone: two passes over the row instead of
+  // the four below. Otherwise the estimate is dropped (nothing is decided by
+  // it) and the full passes follow.
+  if (linear && E > kCandCap && 2 * k <= kCandCap && n_smp > 0u) {
+    const int target = (k + kCandCap) / 2 < 2 * k ? (k + kCandCap) / 2 : 2 * k;
+    const int64_t mm = ((int64_t)n_smp * target + E - 1) / E;
+    const int m = mm < 1 ? 1 : (mm > (int64_t)n_smp ? (int)n_smp : (int)mm);
+    uint32_t b0;
+    int a0, i0;
+    radix_pass<NT>(
+        sm, m, [&](auto add) { if (smp != 0u) add(vbin(smp)); }, b0, a0, i0);
+    const uint32_t thr0 =
+        first_key_in_bin_near(kmin - 1u, kmax, b0, bin_edge_key(b0, h0, scale), vbin);
+    uint32_t n0 = 0; // this wave's keys >= thr0 (key 0, past the row, is below thr0)
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) n0 += (uint32_t)__popcll(__ballot(key[i] >= thr0));
+    // red was last read before radix_pass's final barrier
+    if (lane == 0) sm.red[wave] = n0;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? sm.red[w] : 0u;
+      total += sm.red[w];
+    }
+    if (total >= (uint32_t)k && total <= (uint32_t)kCandCap) {
+      uint32_t at = before;
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const bool c = key[i] >= thr0;
+        const uint64_t mk = __ballot(c);
+        if (c) {
+          const uint32_t q = at + (uint32_t)lanes_below(mk);
+          sm.cand[q] = key[i];
+          sm.cidx[q] = (uint32_t)(base + 64 * i + lane);
+        }
+        at += (uint32_t)__popcll(mk);
+      }
+      __syncthreads();
+      compacted = true;
+      in_lds = true;
+      nc = (int)total;
+      cand = (int)total;
+      lo = thr0;
+    }
+  }
+
+  // ---- pass 1 over every key, by value bin
+  if (linear && !compacted) {
     uint32_t bin;
     int above, inbin;
     radix_pass<NT>(
@@ -444,56 +582,25 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   const bool all_ties = need_eq == 0 || need_eq == n_eq_total;
   const uint32_t thr_ge = need_eq == 0 ? thr + 1u : thr;
 
-  // ---- counting pass: per wave, keys taken wholesale and keys == thr
-  uint32_t n_gt = 0, n_eq = 0;
-  if (all_ties) {
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) n_gt += __popcll(__ballot(key[i] >= thr_ge));
+  if (compacted) {
+    // over the compacted keys: wave w owns entries [w * run, w * run + run)
+    constexpr int NQ = kCandCap / NT; // runs of 64 per wave (run <= kCandCap / NW)
+    static_assert(kCandCap % NT == 0, "whole runs per wave");
+    const int run = (((nc + NW - 1) / NW) + 63) & ~63;
+    const int j0 = wave * run + lane;
+    emit_selection<NT, NQ>(
+        sm,
+        [&](int q) -> uint32_t {
+          const int j = j0 + 64 * q;
+          return 64 * q < run && j < nc ? sm.cand[j] : 0u;
+        },
+        [&](int q) -> int32_t { return ib + (int32_t)sm.cidx[j0 + 64 * q]; }, thr, need_eq,
+        all_ties, thr_ge, k, out);
   } else {
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) { // key 0 (past the row) never reaches thr
-      n_gt += __popcll(__ballot(key[i] > thr));
-      n_eq += __popcll(__ballot(key[i] == thr));
-    }
-  }
-  __syncthreads(); // every thread is done reading red and sel
-  if (lane == 0) {
-    sm.red[wave] = n_gt;
-    sm.red[16 + wave] = n_eq;
-  }
-  __syncthreads();
-  int gt_before = 0, eq_before = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    gt_before += w < wave ? (int)sm.red[w] : 0;
-    eq_before += w < wave ? (int)sm.red[16 + w] : 0;
-  }
-
-  // ---- writing pass in index order
-  if (all_ties) {
-    int pos = gt_before;
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      const bool sel = key[i] >= thr_ge;
-      const uint64_t msel = __ballot(sel);
-      const int p = pos + lanes_below(msel);
-      if (sel && p < k) out[p] = ib + base + i * 64 + lane;
-      pos += (int)__popcll(msel);
-    }
-  } else {
-    int pos = gt_before + (eq_before < need_eq ? eq_before : need_eq);
-    int eq_seen = eq_before;
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      const bool eq = key[i] == thr;
-      const uint64_t meq = __ballot(eq);
-      const bool sel = key[i] > thr || (eq && eq_seen + lanes_below(meq) < need_eq);
-      const uint64_t msel = __ballot(sel);
-      const int p = pos + lanes_below(msel);
-      if (sel && p < k) out[p] = ib + base + i * 64 + lane;
-      pos += (int)__popcll(msel);
-      eq_seen += (int)__popcll(meq);
-    }
+    emit_selection<NT, IPT>(
+        sm, [&](int i) -> uint32_t { return key[i]; },
+        [&](int i) -> int32_t { return ib + base + i * 64 + lane; }, thr, need_eq, all_ties,
+        thr_ge, k, out);
   }
 }
 
