@@ -246,6 +246,53 @@ def test_topk_wave_kernel_adversarial_rows_exact(k):
         check_topk_exact(o[r], vals[r], int(E[r]), k, "k=%d row %d (E=%d)" % (k, r, E[r]))
 
 
+def _sampled_positions(E, NT=1024):
+    """Row positions whose keys the wide-row selection samples for its
+    threshold estimate: wave w of the NT / 64 waves owns the run
+    [w * rounds * 64, ...), rounds = ceil(E / NT), and lane l samples item
+    l % rounds of that run."""
+    rounds = -(-E // NT)
+    w = np.arange(NT // 64)[:, None]
+    lane = np.arange(64)[None, :]
+    p = (w * rounds * 64 + 64 * (lane % rounds) + lane).ravel()
+    return p[p < E]
+
+
+@pytest.mark.parametrize("k", [64, 700, 2048])
+def test_topk_wide_rows_every_threshold_path_exact(k):
+    """Rows wider than 4096 scores (one work group per row, keys estimated
+    from a sample): families that take each branch of the estimate -- keys
+    above it compacted and selected with every tie taken (normal scores) or
+    only some (runs of equal scores), too many keys above it (heavy ties, a
+    crowded bin under far outliers) and too few (the sampled positions hold
+    the largest scores) -- at several lengths; every row exact against the
+    oracle's top-k of the same fp32 values."""
+    log("topk wide rows k %d" % k)
+    W = 65536
+    rng = np.random.default_rng(9000 + k)
+    vals, E = [], []
+    for e in (4097, 20000, 32768, 65536):
+        fams = _adversarial_rows(W, rng)
+        boosted = rng.standard_normal(W).astype(np.float32)
+        boosted[_sampled_positions(e)] += 100.0
+        fams.append(boosted)
+        for row in fams:
+            vals.append(row)
+            E.append(e)
+    vals = np.stack(vals)
+    E = np.array(E, dtype=np.int32)
+    dev = torch.from_numpy(vals).cuda()
+    lens = torch.from_numpy(E).cuda()
+    out = torch.empty((len(E), k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(len(E), dtype=torch.int32, device="cuda")
+    idx.idx_topk(dev, W, lens, len(E), 1, k, out, cnt)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(cnt.cpu().numpy(), np.minimum(E, k))
+    for r in range(len(E)):
+        check_topk_exact(o[r], vals[r], int(E[r]), k, "k=%d row %d (E=%d)" % (k, r, E[r]))
+
+
 def test_topk_all_equal_and_two_values():
     W, k = 3000, 100
     rows = np.zeros((3, W), dtype=np.float32)
