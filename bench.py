@@ -394,91 +394,135 @@ def summarize_trace(trace_dir, out_md, title, command, scoring_groups=None):
     log("wrote " + out_md)
 
 
-def summarize_mfma(pmc_dir):
-    """MFMA use of the prefill scoring kernel from one rocprofv3 run with
-    --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
-    of `--prefill-counters`: FP8 flops per dispatch = MFMA instructions x
-    16*16*128*2, over that dispatch's traced duration."""
+PREFILL_PMC_PASSES = (
+    # rocprofv3 collects one pass per run: at most 8 SQ and 2 GRBM counters each
+    "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU "
+    "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_SCA "
+    "SQ_WAIT_INST_LDS SQ_WAVES GRBM_GUI_ACTIVE",
+)
+N_XCD = 8     # GRBM_GUI_ACTIVE is summed over the eight XCDs
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+
+
+def summarize_mfma(pmc_dirs):
+    """Counters of the prefill scoring kernel from rocprofv3 runs of
+    `--prefill-counters`, one per counter pass (PREFILL_PMC_PASSES, each with
+    --kernel-trace), matched by the order of the prefill dispatches: FP8 flops
+    per dispatch = MFMA instructions x 16*16*128*2 over the traced duration,
+    the engine clock from GRBM_GUI_ACTIVE, and per SIMD the MFMA busy share
+    and VALU / LDS / SALU instructions per MFMA."""
     import csv
     import glob
 
-    def one(pattern):
-        files = glob.glob(os.path.join(pmc_dir, "**", pattern), recursive=True)
+    def one(d, pattern):
+        files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
         if not files:
-            raise SystemExit("no %s under %s" % (pattern, pmc_dir))
+            raise SystemExit("no %s under %s" % (pattern, d))
         with open(files[0]) as fh:
             return list(csv.DictReader(fh))
 
-    cnt = {}
-    for r in one("*counter_collection.csv"):
-        if "prefill_logits_kernel" not in r["Kernel_Name"]:
-            continue
-        d = cnt.setdefault(int(r["Dispatch_Id"]), {})
-        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    dur = {}
-    for r in one("*kernel_trace.csv"):
-        if "prefill_logits_kernel" in r["Kernel_Name"]:
-            dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    rows = []
-    for did in sorted(cnt):
-        if did not in dur:
-            continue
-        c = cnt[did]
-        flops = c.get("SQ_INSTS_MFMA", 0.0) * FP8_MFMA_FLOPS
-        rows.append({"dispatch": did, "mfma_insts": c.get("SQ_INSTS_MFMA", 0.0),
-                     "mfma_busy_cycles": c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0),
-                     "grbm_gui_active": c.get("GRBM_GUI_ACTIVE", 0.0),
-                     "us": dur[did] * 1e6, "tflops": flops / dur[did] / 1e12})
-    big = rows  # every chunk's dispatch of every call
-    tot = lambda key: sum(r[key] for r in big)
-    # Aggregates over all dispatches: flops and busy cycles over the summed
-    # traced durations. MFMA busy cycles are summed over the 1024 SIMDs (one
-    # 16x16x128 FP8 MFMA keeps a SIMD busy 32 cycles); against the traced
-    # duration at the 2.4 GHz peak engine clock this is a lower bound on the
-    # busy fraction.
-    agg_tflops = tot("mfma_insts") * FP8_MFMA_FLOPS / (tot("us") * 1e-6) / 1e12
-    busy_frac = tot("mfma_busy_cycles") / (1024 * tot("us") * 1e-6 * 2.4e9)
-    avg = lambda key: tot(key) / len(big)
+    merged = None
+    for d in pmc_dirs:
+        cnt = {}
+        for r in one(d, "*counter_collection.csv"):
+            if "prefill_logits_kernel" not in r["Kernel_Name"]:
+                continue
+            e = cnt.setdefault(int(r["Dispatch_Id"]), {})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        dur = {}
+        for r in one(d, "*kernel_trace.csv"):
+            if "prefill_logits_kernel" in r["Kernel_Name"]:
+                dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        rows = [dict(cnt[i], us=dur[i] * 1e6, chunk=n % 2) for n, i in enumerate(sorted(cnt)) if i in dur]
+        if merged is None:
+            merged = rows
+        else:
+            if len(rows) != len(merged):
+                raise SystemExit("%s has %d prefill dispatches, the first run %d" % (d, len(rows), len(merged)))
+            for a, b in zip(merged, rows):
+                a.update({k: v for k, v in b.items() if k not in ("us", "chunk")})
+    big = merged
+    for r in big:
+        r["tflops"] = r.get("SQ_INSTS_MFMA", 0.0) * FP8_MFMA_FLOPS / (r["us"] * 1e-6) / 1e12
+    tot = lambda key, rows=big: sum(r.get(key, 0.0) for r in rows)
+    agg_tflops = tot("SQ_INSTS_MFMA") * FP8_MFMA_FLOPS / (tot("us") * 1e-6) / 1e12
+    busy_frac = tot("SQ_VALU_MFMA_BUSY_CYCLES") / (N_SIMD * tot("us") * 1e-6 * 2.4e9)
+
+    def derived(rows):
+        us = tot("us", rows)
+        cycles = tot("GRBM_GUI_ACTIVE", rows) / N_XCD  # engine cycles of the dispatches
+        mfma = tot("SQ_INSTS_MFMA", rows)
+        valu = tot("SQ_INSTS_VALU", rows) - mfma  # SQ_INSTS_VALU counts the MFMAs too
+        return {
+            "us": us,
+            "clock_ghz": cycles / (us * 1e-6) / 1e9 if us else 0.0,
+            "fp8_tflops": mfma * FP8_MFMA_FLOPS / (us * 1e-6) / 1e12 if us else 0.0,
+            # one 16x16x128 FP8 MFMA keeps its SIMD's matrix core 32 cycles
+            "mfma_busy_frac": 32.0 * mfma / (N_SIMD * cycles) if cycles else 0.0,
+            "valu_per_mfma": valu / mfma if mfma else 0.0,
+            "lds_per_mfma": tot("SQ_INSTS_LDS", rows) / mfma if mfma else 0.0,
+            "salu_per_mfma": tot("SQ_INSTS_SALU", rows) / mfma if mfma else 0.0,
+            # quad-cycles summed over waves, as a share of SIMD cycles
+            "valu_active_frac": 4.0 * tot("SQ_ACTIVE_INST_VALU", rows) / (N_SIMD * cycles) if cycles else 0.0,
+            "lds_bank_conflicts_per_lds_inst": tot("SQ_LDS_BANK_CONFLICT", rows) / tot("SQ_INSTS_LDS", rows)
+            if tot("SQ_INSTS_LDS", rows) else 0.0,
+            # a wave's alive time over its dispatch's duration, averaged
+            "wave_alive_frac": 4.0 * tot("SQ_WAVE_CYCLES", rows) / tot("SQ_WAVES", rows) / (cycles / len(rows))
+            if tot("SQ_WAVES", rows) and cycles else 0.0,
+        }
+
+    per_chunk = {c: derived([r for r in big if r["chunk"] == c]) for c in (0, 1)}
     summary = {
         "kernel": "prefill_logits_kernel<FP8, 4 tiles> (both chunks: 8192 + 8192 rows)",
         "workload": "chunked prefill: 16384 rows over 4096 keys, causal (r+1)//4, page 64",
         "kernel_source_digest": prefill_source_digest(),
-        "commands": [
-            "rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
-            "--kernel-trace --output-format csv -d <dir> -o run -- "
-            "python3 -u bench.py --prefill-counters",
-            "python3 bench.py --summarize-mfma <dir>",
-        ],
+        "commands": ["rocprofv3 --pmc %s --kernel-trace --output-format csv -d <dir%d> -o run -- "
+                     "python3 -u bench.py --prefill-counters" % (c, n + 1)
+                     for n, c in enumerate(PREFILL_PMC_PASSES)] +
+                    ["python3 bench.py --summarize-mfma %s" % " ".join(
+                        "<dir%d>" % (n + 1) for n in range(len(PREFILL_PMC_PASSES)))],
         "dispatches": big,
-        "mfma_insts_per_dispatch": avg("mfma_insts"),
-        "us_per_dispatch": avg("us"),
+        "us_per_dispatch": tot("us") / len(big),
         "fp8_tflops": agg_tflops,
         "fp8_mfma_frac": agg_tflops / FP8_MFMA_PEAK_TFLOPS,
         "mfma_busy_frac_at_2p4ghz": busy_frac,
+        "per_chunk": {"short rows (0-2048 keys)": per_chunk[0], "long rows (2048-4096 keys)": per_chunk[1]},
     }
     with open(MFMA_SUMMARY + ".json", "w") as fh:
         json.dump(summary, fh, indent=1)
+    names = [n for n in PREFILL_PMC_PASSES[0].split() + PREFILL_PMC_PASSES[1].split()]
+    names = [n for i, n in enumerate(names) if n not in names[:i]]
     with open(MFMA_SUMMARY + ".md", "w") as fh:
-        fh.write("# MFMA use of the chunked-prefill scoring kernel (rocprofv3 PMC)\n\n")
-        fh.write("Commands (repository root, one MI355X):\n\n```\n%s\n```\n\n" %
+        fh.write("# Pipe use of the chunked-prefill scoring kernel (rocprofv3 PMC)\n\n")
+        fh.write("Commands (repository root, one MI355X; one counter pass per run):\n\n```\n%s\n```\n\n" %
                  "\n".join(summary["commands"]))
-        fh.write("`bench.py --prefill-counters` runs the 16384-row prefill call three times "
-                 "(budget 256e6 B: two chunks of 8192 rows; the first sees 0-2048 keys per row, "
-                 "the second 2048-4096). Rows below are every chunk's dispatch.\n\n")
-        fh.write("| dispatch | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | "
-                 "traced us | FP8 TFLOP/s |\n|---|---|---|---|---|---|\n")
-        for r in big:
-            fh.write("| %d | %s | %s | %s | %.1f | %.0f |\n" % (
-                r["dispatch"], f"{r['mfma_insts']:,.0f}", f"{r['mfma_busy_cycles']:,.0f}",
-                f"{r['grbm_gui_active']:,.0f}", r["us"], r["tflops"]))
-        fh.write("\nFP8 flops = SQ_INSTS_MFMA x %d (one 16x16x128 FP8 MFMA); summed over all "
-                 "dispatches and divided by their summed traced durations: %.0f "
-                 "TFLOP/s = %.1f%% of the 5.0 PFLOP/s dense FP8 peak. SQ_VALU_MFMA_BUSY_CYCLES "
-                 "over 1024 SIMDs x traced duration x 2.4 GHz: %.1f%% busy (a lower bound if the "
-                 "engine clock ran below 2.4 GHz). GRBM_GUI_ACTIVE is listed as read. Kernel "
-                 "source digest: `%s`.\n" % (
-                     FP8_MFMA_FLOPS, summary["fp8_tflops"], 100 * summary["fp8_mfma_frac"],
-                     100 * busy_frac, summary["kernel_source_digest"]))
+        fh.write("`bench.py --prefill-counters` runs the 16384-row chunked prefill call (budget 256e6 B: "
+                 "two chunks of 8192 rows; the first sees 0-2048 keys per row, the second 2048-4096). "
+                 "Counters are summed over all XCDs and SIMDs; the runs' dispatches are matched in "
+                 "order.\n\n")
+        fh.write("| dispatch | chunk | traced us | FP8 TFLOP/s | " + " | ".join(names) + " |\n")
+        fh.write("|---" * (4 + len(names)) + "|\n")
+        for n, r in enumerate(big):
+            fh.write("| %d | %d | %.1f | %.0f | %s |\n" % (
+                n, r["chunk"], r["us"], r["tflops"],
+                " | ".join(f"{r.get(k, 0.0):,.0f}" for k in names)))
+        fh.write("\n## Derived, per chunk\n\n| | short rows | long rows |\n|---|---|---|\n")
+        labels = [("traced us (sum)", "us", "%.1f"), ("engine clock, GHz (GRBM_GUI_ACTIVE / 8 / time)", "clock_ghz", "%.2f"),
+                  ("FP8 TFLOP/s", "fp8_tflops", "%.0f"),
+                  ("MFMA busy share of SIMD cycles (32 cycles per MFMA)", "mfma_busy_frac", "%.3f"),
+                  ("VALU instructions per MFMA (SQ_INSTS_VALU less the MFMAs)", "valu_per_mfma", "%.2f"),
+                  ("VALU active share of SIMD cycles (4 x SQ_ACTIVE_INST_VALU)", "valu_active_frac", "%.3f"),
+                  ("LDS instructions per MFMA", "lds_per_mfma", "%.3f"),
+                  ("SALU instructions per MFMA", "salu_per_mfma", "%.2f"),
+                  ("LDS bank conflicts per LDS instruction", "lds_bank_conflicts_per_lds_inst", "%.3f"),
+                  ("wave-alive share of the dispatch (4 x SQ_WAVE_CYCLES / SQ_WAVES / cycles)", "wave_alive_frac", "%.3f")]
+        for lab, key, fmt in labels:
+            fh.write("| %s | %s | %s |\n" % (lab, fmt % per_chunk[0][key], fmt % per_chunk[1][key]))
+        fh.write("\nAll dispatches: %.0f TFLOP/s = %.1f%% of the 5.0 PFLOP/s dense FP8 peak. Kernel source "
+                 "digest: `%s`.\n" % (agg_tflops, 100 * agg_tflops / FP8_MFMA_PEAK_TFLOPS,
+                                       summary["kernel_source_digest"]))
+    log("wrote " + MFMA_SUMMARY + ".md")
     print(json.dumps({k: v for k, v in summary.items() if k != "dispatches"}, indent=1))
 
 
@@ -794,7 +838,7 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--prefill-counters", action="store_true",
                     help="eager prefill calls only (for rocprofv3 --pmc)")
-    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR", nargs="+",
                     help="write the profiles/ MFMA summary from a --prefill-counters PMC run")
     ap.add_argument("--counters", action="store_true",
                     help="only a reference copy + scoring launches, for rocprofv3 --pmc runs")

@@ -25,9 +25,12 @@ __host__ __device__ inline int32_t clamp_seg_len(int32_t v) {
 }
 constexpr int kPrefillRowsPerSeg = 7;  // query rows sharing one K stream in prefill
 // Work-split cost of entering a segment, in key blocks: a prefill row block
-// reloads seven query rows (about one block's scoring time); a decode
-// sequence's query load hides under the key stream.
-constexpr int kPrefillEntryCost = 1;
+// reloads seven query rows and their lengths, a wait of about three blocks'
+// scoring time (per-group timestamps: the groups whose ranges hold many short
+// segments finished last with a cost of 1; 3 takes 1.5-2% off the longer
+// chunk of the 16384-row prefill); a decode sequence's query load hides
+// under the key stream.
+constexpr int kPrefillEntryCost = 3;
 constexpr int kDecodeEntryCost = 0;
 
 // Tokens per schedule block: a block never straddles two pages.
