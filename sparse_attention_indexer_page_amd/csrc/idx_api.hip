@@ -258,7 +258,7 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
   a.row0 = 0;
   a.row_end = 0;
   a.block_tokens = idx::block_tokens(page_size);
-  a.entry_cost = idx::kDecodeEntryCost;
+  a.entry_cost = idx::decode_entry_cost(next_n, a.block_tokens);
   a.n_ctas = n_ctas;
   a.cta_info = cta_info;
   a.n_chunks = 1;

@@ -208,6 +208,7 @@ __device__ inline int32_t wave_incl_scan(int32_t v) {
 __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   constexpr int kChunks = kInlineSplitMaxSegs / 64;
   const int lane = threadIdx.x & 63;
+  const int32_t entry = decode_entry_cost(a.next_n, a.block_tokens); // as the schedule builder
   int32_t len[kChunks];
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) // every load first: one round trip
@@ -219,7 +220,7 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
     if (i * 64 < a.nseg) {
       const int32_t L = len[i]; // clamped to [0, kMaxSegLen]
       const int32_t nb = (L + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens); // 32 or 64
-      const int32_t cost = nb > 0 ? nb + kDecodeEntryCost : 0;
+      const int32_t cost = nb > 0 ? nb + entry : 0;
       const int32_t incl = wave_incl_scan(cost);
       pre[i] = total + incl - cost;
       total += __builtin_amdgcn_readlane(incl, 63);
@@ -250,7 +251,7 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
           p = __builtin_amdgcn_readlane(pre[i], seg & 63);
           if (e == 0) len0 = __builtin_amdgcn_readlane(len[i], seg & 63);
         }
-      const int64_t u = T - p - kDecodeEntryCost;
+      const int64_t u = T - p - entry;
       blk = u > 0 ? (int32_t)u : 0;
     }
     if (e == 0) {
