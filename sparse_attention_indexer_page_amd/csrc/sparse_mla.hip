@@ -28,9 +28,10 @@
 //   * online softmax per head over the block; the scores come out of that
 //     MFMA in the A-operand layout of the P.V product (lane l: head l & 15,
 //     k-slots 8g..8g+7 = tokens 4g..4g+3 of both tiles), so P needs no
-//     shuffle, only bf16 rounding;
+//     shuffle, only its split into a bf16 part and a bf16 remainder;
 //   * O += P V on v_mfma_f32_16x16x32_bf16 (heads x 16 dims, K = the 32
-//     tokens), 16 tiles for the wave's 256 dims, fp32 accumulators in VGPRs;
+//     tokens), two products per tile (the two parts of P), 16 tiles for the
+//     wave's 256 dims, fp32 accumulators in VGPRs;
 //     a lane reads 8-byte runs of 4 dims per token and byte-permutes them
 //     into the token-major B operands of 4 tiles (a tile's 16 columns are
 //     then every fourth dim), rather than reading 2-byte columns.
@@ -153,11 +154,19 @@ __device__ inline void score_block(const MlaArgs &a, MlaState &S, const uint8_t 
   float ah[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) ah[jj] = __shfl(alpha, 4 * g + jj, 64);
-  // P as the A operand of the 16x16x32 product: head col, k-slots 8g..8g+7
-  v8bf pa;
+  // P as the A operand of the 16x16x32 product: head col, k-slots 8g..8g+7.
+  // Each probability is split into its bf16 rounding and the bf16 rounding
+  // of the remainder, and both parts multiply V: together they carry p to
+  // about 2^-16 relative instead of bf16's 2^-8, so the output's only
+  // sizeable error is its own final bf16 rounding.
+  v8bf pa, pl;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    pa[i] = __builtin_bit_cast(__bf16, (uint16_t)bf16_rne(p[i >> 2][i & 3]));
+  for (int i = 0; i < 8; ++i) {
+    const float pv = p[i >> 2][i & 3];
+    const uint32_t h = bf16_rne(pv);
+    pa[i] = __builtin_bit_cast(__bf16, (uint16_t)h);
+    pl[i] = __builtin_bit_cast(__bf16, (uint16_t)bf16_rne(pv - __uint_as_float(h << 16)));
+  }
   // V operands: lane col reads 8 bytes (dims 4 col .. + 3 of a 64-dim
   // span) of each of its 8 tokens and regroups them into the B operands of
   // four tiles, tile j taking dim 4 col + j of every token (two tokens per
@@ -183,6 +192,7 @@ __device__ inline void score_block(const MlaArgs &a, MlaState &S, const uint8_t 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) o[jj] *= ah[jj];
       o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(v8bf, vb), o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, __builtin_bit_cast(v8bf, vb), o, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0); // the V reads of one 64-dim span in flight
   }

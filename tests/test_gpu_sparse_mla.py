@@ -1,6 +1,6 @@
 """Sparse attention over the selected tokens on the GPU against the oracle:
-bf16 outputs within the bf16 error bound of the oracle's double-precision
-result, the log-sum-exp, skipped entries, empty rows, page sizes and row
+bf16 outputs within half a bf16 ulp of the oracle's double-precision result
+(plus the fp32 sums' share), the log-sum-exp, skipped entries, empty rows, page sizes and row
 strides, and a full-size batch on sampled rows."""
 import numpy as np
 import pytest
@@ -44,6 +44,8 @@ def _check(case, scale, got, got_lse, rows=None):
                                      case.page_size, case.num_pages, case.block_tables,
                                      case.next_n, case.indices, case.topk_lens, scale)
     rows = range(case.R) if rows is None else rows
+    # the largest |latent value| in the cache (its bf16 rows; padding is 0)
+    cmax = float(np.abs((case.data.view(np.uint16).astype(np.uint32) << 16).view(np.float32)).max())
     for r in rows:
         n = int(case.topk_lens[r])
         if n == 0 or np.all(case.indices[r, :n] < 0):
@@ -51,11 +53,14 @@ def _check(case, scale, got, got_lse, rows=None):
             if got_lse is not None:
                 assert np.all(np.isneginf(got_lse[r]))
             continue
-        # bf16 probabilities (2^-9 relative) against the value scale, bf16 output
-        vmax = np.abs(ref[r]).max() + 1.0
+        # The output's own bf16 rounding (half an ulp: 2^-8 relative), plus
+        # what the fp32 sums over at most 2048 tokens and the probabilities
+        # (carried to ~2^-16 by two bf16 parts) can add, against the largest
+        # latent value |c|: 2048 * 2^-24 + 2^-16 < 2e-4.
         err = np.abs(got[r] - ref[r])
-        bound = 4e-3 * vmax + 8e-3 * np.abs(ref[r])
-        assert np.all(err <= bound), "row %d: max err %.3e" % (r, err.max())
+        bound = 2.0 ** -8 * np.abs(ref[r]) + 2e-4 * cmax
+        assert np.all(err <= bound), "row %d: max err %.3e, worst err/bound %.3f" % (
+            r, err.max(), (err / bound).max())
         if got_lse is not None:
             assert np.allclose(got_lse[r], ref_lse[r], rtol=1e-4, atol=1e-3), "row %d lse" % r
 
