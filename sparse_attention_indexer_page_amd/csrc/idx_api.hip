@@ -259,6 +259,7 @@ idx_status idx_build_schedule(const int32_t *context_lens, int32_t B, int32_t ne
   a.row_end = 0;
   a.block_tokens = idx::block_tokens(page_size);
   a.entry_cost = idx::decode_entry_cost(next_n, a.block_tokens);
+  a.skip_len = 0; // decode scores are the call's output: every sequence is scored
   a.n_ctas = n_ctas;
   a.cta_info = cta_info;
   a.n_chunks = 1;
@@ -609,6 +610,7 @@ static idx_status prefill_chunked_topk(const idx_query *q, const idx_kv_cache *k
   sa.row_end = T;
   sa.block_tokens = idx::block_tokens(kv->page_size);
   sa.entry_cost = idx::kPrefillEntryCost;
+  sa.skip_len = k; // rows seeing at most k keys select them all: no scores needed
   sa.n_ctas = n_ctas;
   sa.cta_info = cta_scratch;
   sa.n_chunks = (int32_t)n_chunks;
@@ -623,6 +625,7 @@ static idx_status prefill_chunked_topk(const idx_query *q, const idx_kv_cache *k
   la.bt_cols = (W + kv->page_size - 1) / kv->page_size;
   la.lens = visible_end;
   la.next_n = 1;
+  la.skip_len = k;
   la.n_ctas = n_ctas;
   la.logits = logits_scratch;
   la.W = W;

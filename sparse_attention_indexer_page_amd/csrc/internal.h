@@ -47,7 +47,8 @@ inline int block_tokens(int page_size) { return page_size < 64 ? page_size : 64;
 enum SegMode : int {
   kSegDecode = 0,  // segment = sequence; length = context_lens[s]
   kSegPrefill = 1, // segment = kPrefillRowsPerSeg consecutive query rows;
-                   // length = max visible_end over those rows
+                   // length = max visible_end over those rows, or 0 when that
+                   // is at most skip_len (every row then selects all its keys)
 };
 
 struct ScheduleArgs {
@@ -58,6 +59,7 @@ struct ScheduleArgs {
   int32_t row_end;    // prefill: one past the last query row of the chunk
   int32_t block_tokens;
   int32_t entry_cost; // cost of entering a non-empty segment, in blocks
+  int32_t skip_len;   // prefill: a segment of length <= skip_len has no blocks (0: none skipped)
   int32_t n_ctas;
   int32_t *cta_info; // [n_ctas + 1][2]
   // prefill: work group g builds the schedule of rows [row0 + g*chunk_rows,
@@ -94,6 +96,8 @@ struct LogitsArgs {
   int32_t row_cap;             // decode varlen: rows the query and logits buffers hold
   int32_t row0;                // prefill: first row of the chunk
   int32_t row_end;             // prefill: end row of the chunk
+  int32_t skip_len;            // prefill: a row block whose rows all see at most this many
+                               // keys is not scored (its top-k is every visible key)
   const int32_t *cta_info;
   int32_t n_ctas;
   // output

@@ -85,7 +85,10 @@ __device__ inline int32_t block_length(const LogitsArgs &a, int s) {
       L = e > L ? e : L;
     }
   }
-  return clamp_seg_len(L);
+  L = clamp_seg_len(L);
+  // a block whose rows all select every visible key needs no scores (the
+  // schedule builder applies the same rule)
+  return L <= a.skip_len ? 0 : L;
 }
 
 __device__ inline bool in_range(const LogitsArgs &a, const Walk &w) {

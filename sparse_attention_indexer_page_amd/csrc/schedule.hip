@@ -39,7 +39,8 @@ __device__ inline int32_t segment_length(const ScheduleArgs &a, int s) {
       m = v > m ? v : m;
     }
   }
-  return clamp_seg_len(m);
+  m = clamp_seg_len(m);
+  return m <= a.skip_len ? 0 : m; // rows that select all their keys need no scores
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
