@@ -281,6 +281,9 @@ int64_t idx_prefill_schedule_ints(int32_t T, int64_t W, int64_t budget_bytes);
  * One launch builds every chunk's schedule (each encodes its chunk's absolute
  * rows, in its own part of cta_scratch); the host loop over chunks then
  * enqueues scores and top-k per chunk on `stream` without synchronizing.
+ * A row that sees at most k keys selects all of them, so it needs no scores:
+ * blocks of rows that all do are not scored, and logits_scratch is workspace
+ * whose rows for them are left as they were.
  * Errors: as idx_paged_mqa_logits and idx_topk; IDX_ERR_WORKSPACE when a
  * scratch buffer is too small.
  */
