@@ -146,19 +146,19 @@ struct Row {
   v8i a[4];       // A operands of the four head tiles
   int32_t asc[4]; // MXFP4 E8M0 scale of the lane's block
   float w[4][4];  // weights of the lane's 16 heads (times the FP8 q scale)
-  int32_t E;      // visible length
-  int32_t out;    // logits row, or -1
+  int32_t lim;    // tokens of the row stored: min(visible length, W); 0 for a padding row
+  float *orow;    // the row's logits (wave-uniform, so the store address is scalar + lane)
 };
 
 template <int DT> __device__ inline void enter_block(const LogitsArgs &a, int s, Row &R) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int hl = lane & 15;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = a.row0 + s * kRowsPerGroup + wave;
   if (r >= a.row_end) {
-    R.E = 0;
-    R.out = -1;
+    R.lim = 0;
+    R.orow = a.logits;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       R.a[m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -169,8 +169,11 @@ template <int DT> __device__ inline void enter_block(const LogitsArgs &a, int s,
     return;
   }
   const int32_t e = uniform_load(a.lens + r);
-  R.E = e > 0 ? e : 0;
-  R.out = r - a.row0;
+  // the block's length is the clamped maximum over its rows, so this never
+  // passes the last block scored
+  const int32_t ec = clamp_seg_len(e);
+  R.lim = ec < a.W ? ec : (int32_t)a.W;
+  R.orow = a.logits + (int64_t)(r - a.row0) * a.W;
   float qs = 1.f;
   if (DT == IDX_FP8_E4M3 && a.q_scale != nullptr) qs = uniform_load(reinterpret_cast<const float *>(a.q_scale) + r);
   const float *wrow = a.weights + (int64_t)r * kHeads;
@@ -198,8 +201,7 @@ template <int DT> __device__ inline void enter_block(const LogitsArgs &a, int s,
 
 // Compute wave: scores of one staged key block against its row.
 template <int DT, int TPB>
-__device__ inline void score_stage(const LogitsArgs &a, const Row &R, const uint8_t *stage, int t0,
-                                   int32_t L) {
+__device__ inline void score_stage(const Row &R, const uint8_t *stage, int t0) {
   using S = Stage<DT, TPB>;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -250,8 +252,7 @@ __device__ inline void score_stage(const LogitsArgs &a, const Row &R, const uint
   if (DT == IDX_FP8_E4M3) v *= *reinterpret_cast<const float *>(stage + S::kData + 4 * tl);
   const int t = t0 + tl;
   const bool holder = TPB == 4 || (g & 1) == 0;
-  if (holder && R.out >= 0 && t < L && t < R.E && t < a.W)
-    a.logits[(int64_t)R.out * a.W + t] = v;
+  if (holder && t < R.lim) R.orow[t] = v;
 }
 
 template <int DT, int TPB>
@@ -285,7 +286,6 @@ __global__ __launch_bounds__(kWaves * 64, 4) void prefill_logits_kernel(LogitsAr
     }
   }
   Row R;
-  int32_t L = block_length(a, w.s);
   if (!loader) enter_block<DT>(a, w.s, R);
 
   // Group i scores blocks [i G, i G + G) from their slots. Before its barrier
@@ -304,16 +304,13 @@ __global__ __launch_bounds__(kWaves * 64, 4) void prefill_logits_kernel(LogitsAr
     bool done = false;
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      if (!loader) score_stage<DT, TPB>(a, R, ring[(i * kGroup + u) % kStages], w.blk * a.block_tokens, L);
+      if (!loader) score_stage<DT, TPB>(R, ring[(i * kGroup + u) % kStages], w.blk * a.block_tokens);
       const int s_prev = w.s;
       if (!advance(a, w)) {
         done = true;
         break;
       }
-      if (w.s != s_prev) {
-        L = block_length(a, w.s);
-        if (!loader) enter_block<DT>(a, w.s, R);
-      }
+      if (w.s != s_prev && !loader) enter_block<DT>(a, w.s, R);
     }
     if (done) break;
   }
