@@ -46,6 +46,10 @@ __device__ inline constexpr int waitcnt_vm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// s_waitcnt immediate that waits for every outstanding LDS and scalar-memory
+// operation of the wave (lgkmcnt 0; vmcnt and expcnt left unwaited).
+__device__ inline constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
+
 // Wave-uniform read of launch metadata (lengths, block-table entries, the
 // work schedule) through the scalar cache: a constant-address-space load at a
 // uniform address becomes s_load, counted by lgkmcnt, so waiting for it never

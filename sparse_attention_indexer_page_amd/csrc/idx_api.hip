@@ -232,8 +232,10 @@ int32_t idx_recommended_decode_ctas(int32_t rows, int32_t dtype, int32_t page_si
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  // batched decode, FP8, 64-row pages: 1024 work groups 31.9 us, 2048: 33.4 us;
-  // MTP (32-row pages, two rows) and MXFP4: 2048 beat 1024 by 6% and 19%
+  // batched decode, FP8, 64-row pages: 1024 work groups 29.8 us, 768: 30.7,
+  // 1536: 35.6, 2048: 34.7 (four 8.4 KB ring slots per group: four groups
+  // per CU); MTP (32-row pages, two rows) and MXFP4 (4.3 KB slots, eight
+  // groups per CU): 2048 beat 1024 by 10% and 7%
   const bool big_blocks = dtype == IDX_FP8_E4M3 && idx::block_tokens(page_size) == 64 && next_n == 1;
   int64_t n = (int64_t)cus * (big_blocks ? 4 : 8);
   if (rows > n) n = rows;

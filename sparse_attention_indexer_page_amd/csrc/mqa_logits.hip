@@ -10,11 +10,21 @@
 // contiguous run of (segment, block) items):
 //   * A segment's query rows stay in VGPRs as MFMA A operands: row r, head
 //     tile m (heads 16m..16m+15) is one 16x128 operand, 32 bytes per lane.
-//   * K is streamed straight from HBM into B operands, one 16-token tile per
-//     16x16x128 MFMA; one MFMA therefore yields 16 heads x 16 tokens of full
-//     dot products (head_dim 128 = the MFMA's K). FP8 uses the unscaled
-//     f8f6f4 form; MXFP4 uses the block-scaled form with the E8M0 scale of
-//     each lane's 32-element block as the operand scale.
+//   * K is streamed from HBM into a four-slot LDS ring per wave with
+//     direct-to-LDS buffer loads, three blocks ahead of the block being
+//     scored. Each load instruction fills 1 KB of a slot with whole key rows
+//     (eight FP8 rows, sixteen MXFP4 rows), so every 128-byte line of a dense
+//     page is read by one instruction; the 16-byte chunks of each row are
+//     XOR-swizzled in LDS so that the MFMA operand reads are conflict-free.
+//     Versus streaming each block straight into registers one block ahead
+//     (the operand order then splits every row over two load instructions),
+//     same bits: batched decode 31.0 -> 29.9 us, MTP 43.4 -> 40.4 us, MXFP4
+//     unchanged (63-65 us), measured in one run.
+//   * One 16-token tile per 16x16x128 MFMA; one MFMA therefore yields 16
+//     heads x 16 tokens of full dot products (head_dim 128 = the MFMA's K).
+//     FP8 uses the unscaled f8f6f4 form; MXFP4 uses the block-scaled form
+//     with the E8M0 scale of each lane's 32-element block as the operand
+//     scale.
 //   * A block of BK = min(P, 64) tokens lies in one physical page (DeepGEMM
 //     PR #14: a 64-row tile would straddle two non-contiguous 32-row pages).
 //     Each page gets its own buffer resource whose size is the page's extent,
@@ -30,11 +40,10 @@
 //
 // Operand lane layout (identical for A and B, which is all a full-length dot
 // product needs): lane l serves row/column (l & 15); lane group g = l >> 4
-// holds FP8 bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the 128-byte row,
-// so each of the two 16-byte loads of a 16-row tile reads 64 contiguous bytes
-// per row; for MXFP4 it holds bytes [16g, 16g+16) = elements [32g, 32g+32),
-// exactly one E8M0 block. Accumulator layout of the 16x16 f32 MFMA: lane l
-// holds column (l & 15), rows 4g..4g+3.
+// holds FP8 bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the 128-byte row;
+// for MXFP4 it holds bytes [16g, 16g+16) = elements [32g, 32g+32), exactly
+// one E8M0 block. Accumulator layout of the 16x16 f32 MFMA: lane l holds
+// column (l & 15), rows 4g..4g+3.
 #include "device_common.h"
 #include "internal.h"
 
@@ -265,106 +274,104 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   return len0;
 }
 
-// K operands of one block: TPB tiles of 16 tokens of one page.
-template <int TPB> struct KBlock {
-  v8i kb[TPB];
-  uint32_t ks[TPB]; // MXFP4: E8M0 scale of the lane's block, tile t (byte 0)
-  uint32_t ksr;     // FP8: fp32 scale bits of the token this lane stores
-  int t0;           // first token of the block
+// One slot of a work group's LDS ring: the key rows of one block, packed at
+// the format's row size (128 bytes FP8, 64 bytes MXFP4) with the 16-byte
+// chunks of each row XOR-swizzled, then 64 per-token scale words (FP8 fp32;
+// MXFP4 four E8M0 bytes, one per 32-element block; words past the page read
+// as zeros). Each load instruction fills 1 KB of the image: eight whole FP8
+// rows (sixteen MXFP4 rows), so every 128-byte line of a dense page is read
+// by one instruction.
+template <int DT, int TPB> struct Slot {
+  static constexpr int kRowBytes = DT == IDX_FP8_E4M3 ? 128 : 64;
+  static constexpr int kUnitsPerRow = kRowBytes / 16;
+  static constexpr int kTileBytes = kTile * kRowBytes; // one 16-token tile
+  static constexpr int kData = TPB * kTileBytes;
+  static constexpr int kDataLoads = kData / 1024;
+  static constexpr int kBytes = kData + 256;
+  static constexpr int kLoads = kDataLoads + 1; // load instructions per block
 };
 
-// Key bytes and key scales are read once per launch: the loads carry the
-// non-temporal hint (cache policy nt), so the stream does not displace the
-// small data every launch reuses (lengths, block tables, queries, weights)
-// or the logits the top-k reads next (decode scoring 35.6 -> 33.4 us on the
-// batched-decode workload, measured).
-constexpr int kStream = 2; // buffer-load aux bits: nt
-
-__device__ inline v4i load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
+// Position of chunk c of packed row r within the row: c ^ swizzle(r). Lanes
+// (g, col) of an MFMA operand read chunk g (and g + 4) of rows 16t + col; the
+// swizzle puts those 16 reads on 16 distinct 16-byte bank groups.
+template <int DT> __device__ inline int swizzle(int r) {
+  return DT == IDX_FP8_E4M3 ? (r >> 1) & 7 : (r >> 2) & 3;
 }
 
-__device__ inline uint32_t load4_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStream);
-}
 
 // Physical page of logical page lp of sequence s, or -1 past the table row.
-// A scalar load: waiting for it never waits for the K loads in flight.
-__device__ inline int64_t page_of(const LogitsArgs &a, int s, int lp) {
-  return lp < a.bt_cols ? (int64_t)uniform_load(a.block_tables + (int64_t)s * a.bt_stride + lp) : -1;
+// A scalar load: waiting for it never waits for the K loads in flight. The
+// entry is returned as stored (sign-extended only where it is used, so the
+// load can stay in flight until then).
+__device__ inline int32_t page_of(const LogitsArgs &a, int s, int lp) {
+  return lp < a.bt_cols ? uniform_load(a.block_tables + (int64_t)s * a.bt_stride + lp) : -1;
 }
 
-// Issues the loads of block w.blk of segment w.s. Every tile is loaded, also
-// past the segment's end: those rows are inside the page (or read as zeros
-// through the buffer bound) and are never stored, and unconditional loads keep
-// the wait counts exact so the next block stays in flight during compute.
-// With live == false (no next block) the same loads go through empty buffer
-// resources: they touch no memory and return zeros, and every path through
-// the block loop then has the same number of loads in flight, which keeps the
-// compiler's wait counts partial (a path without them would force it to wait
-// for every load, including the next block's, before the first MFMA).
-// The block's page comes from the caller (pg < 0: nothing to load).
+__device__ inline int32_t block_page(const LogitsArgs &a, const Walk &w) {
+  return page_of(a, w.s, (w.blk * a.block_tokens) >> __builtin_ctz(a.page_size));
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// Buffer resource words (gfx9 raw buffer: base, no stride, size in bytes).
+__device__ inline v4i rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return v4i{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
+}
+
+// Direct-to-LDS loads (16 and 4 bytes per lane): lane l's bytes land at LDS
+// address lds + size * l. Key bytes and key scales are read once per launch,
+// so the loads carry the non-temporal hint (nt): the stream then does not
+// displace the small data every launch reuses (lengths, block tables,
+// queries, weights) or the logits the top-k reads next (register-load
+// kernel, batched decode: scoring 35.6 -> 33.4 us with the hint, measured). Written as inline assembly so
+// that the compiler, which cannot tell which ring slot such a load fills,
+// does not wait for every one of them before each LDS read; the scoring loop
+// waits for exactly the slot it reads. M0 holds the LDS address; no other
+// code of the decode kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm" // m0 in the clobber list
+__device__ inline void lds_load16(v4i r, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds), "v"(off),
+               "s"(r)
+               : "memory", "m0");
+}
+__device__ inline void lds_load4(v4i r, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen nt lds" ::"s"(lds), "v"(off),
+               "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Issues the direct-to-LDS loads of block blk (of page pg; pg < 0: none)
+// into a ring slot: always Slot::kLoads instructions, so the wave's count of
+// outstanding vector-memory operations tells which slots have landed. With
+// no page the loads go through empty buffer resources: they touch no memory
+// and leave zeros. Every row of the block is loaded, also past the
+// segment's end: those rows are inside the page (or read as zeros through
+// the buffer bound) and their scores are never stored.
 template <int DT, int TPB>
-__device__ inline void issue_block_page(const LogitsArgs &a, int blk, int64_t pg,
-                                        KBlock<TPB> &kb) {
+__device__ inline void issue_slot(const LogitsArgs &a, int blk, int32_t pg, uint8_t *slot) {
+  using S = Slot<DT, TPB>;
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  const int col = lane & 15;
   const int P = a.page_size;
   const int t0 = blk * a.block_tokens;
-  const int lp = t0 / P;
-  const int slot0 = t0 - lp * P;
+  const int slot0 = t0 & (P - 1);
   const bool valid = pg >= 0 && pg < a.num_pages;
-  if (!valid) pg = 0;
-  const uint32_t page_bytes = (uint32_t)(P * a.row_stride);
-  const uint32_t scale_bytes = (uint32_t)((P - 1) * a.scale_row_stride + 4);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.kdata + pg * a.page_stride, valid ? page_bytes : 0u);
-  const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(a.kscale + pg * a.scale_page_stride, valid ? scale_bytes : 0u);
-  kb.t0 = t0;
-  if (DT == IDX_FP8_E4M3) {
-    // one scale per lane: the token this lane holds after the head-sum
-    // reduction (t0 + lane for 4-tile blocks, t0 + 16*(g/2) + col for 2-tile)
-    const uint32_t slot = (uint32_t)(slot0 + (TPB == 4 ? lane : 16 * (g >> 1) + col));
-    kb.ksr = load4_stream(sr, slot * (uint32_t)a.scale_row_stride);
-  }
+  const int64_t p = valid ? pg : 0;
+  const v4i kr = rsrc_words(a.kdata + p * a.page_stride, valid ? (uint32_t)(P * a.row_stride) : 0u);
+  const v4i sr = rsrc_words(a.kscale + p * a.scale_page_stride,
+                            valid ? (uint32_t)((P - 1) * a.scale_row_stride + 4) : 0u);
+  const uint32_t rs = (uint32_t)a.row_stride;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)slot;
 #pragma unroll
-  for (int ti = 0; ti < TPB; ++ti) {
-    const uint32_t slot = (uint32_t)(slot0 + ti * kTile + col);
-    const uint32_t off = slot * (uint32_t)a.row_stride;
-    if (DT == IDX_FP8_E4M3) {
-      kb.kb[ti] = cat(load16_stream(kr, off + 16 * g), load16_stream(kr, off + 64 + 16 * g));
-    } else {
-      const v4i lo = load16_stream(kr, off + 16 * g);
-      kb.kb[ti] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-      kb.ks[ti] = load4_stream(sr, slot * (uint32_t)a.scale_row_stride) >> (8 * g);
-    }
+  for (int j = 0; j < S::kDataLoads; ++j) {
+    const int u = 64 * j + lane;       // 16-byte unit of the packed image
+    const int r = u / S::kUnitsPerRow; // its row
+    const int c = (u % S::kUnitsPerRow) ^ swizzle<DT>(r); // the row's chunk stored there
+    lds_load16(kr, base + 1024 * j, (uint32_t)(slot0 + r) * rs + 16 * c);
   }
-}
-
-template <int DT, int TPB>
-__device__ inline void issue_block(const LogitsArgs &a, const Walk &w, bool live, KBlock<TPB> &kb) {
-  const int lp = (w.blk * a.block_tokens) / a.page_size;
-  issue_block_page<DT, TPB>(a, w.blk, live ? page_of(a, w.s, lp) : -1, kb);
-}
-
-// MFMAs of one 16-token tile against every head tile of every row.
-template <int DT, int NROW, int TPB>
-__device__ inline void tile_mfma(const QRegs<DT, NROW> &Q, const KBlock<TPB> &kb, int ti,
-                                 v4f (&acc)[NROW][4]) {
-#pragma unroll
-  for (int i = 0; i < NROW; ++i) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const v4f zero = {0.f, 0.f, 0.f, 0.f};
-      if (DT == IDX_FP8_E4M3)
-        acc[i][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i][m], kb.kb[ti], zero,
-                                                                     kFmtFp8, kFmtFp8, 0, 0, 0, 0);
-      else
-        acc[i][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            Q.a[i][m], kb.kb[ti], zero, kFmtFp4, kFmtFp4, 0, Q.asc[i][m], 0, (int)kb.ks[ti]);
-    }
-  }
+  lds_load4(sr, base + S::kData, (uint32_t)(slot0 + lane) * (uint32_t)a.scale_row_stride);
 }
 
 // Logits of up to kStageTokens consecutive tokens per row (one aligned window
@@ -406,23 +413,57 @@ __device__ inline void flush_stage(const LogitsArgs &a, const QRegs<DT, NROW> &Q
   ss.base = -1;
 }
 
-// Scores of one loaded block against the segment's rows, staged for logits.
-// Tile t+1's MFMAs are issued before tile t's epilogue so the matrix core and
-// the vector ALU overlap. Every tile is computed; tokens past the segment's
-// end (whose keys may be canary bytes) only reach their own columns and are
-// never stored.
+// Scores of one landed ring slot against the segment's rows, staged for
+// logits. Tile t+1's operands are read and its MFMAs issued before tile t's
+// epilogue. Every tile is computed; tokens past the segment's end only reach
+// their own columns and are never stored.
 template <int DT, int NROW, int TPB>
-__device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q, int32_t L,
-                                   const KBlock<TPB> &kb, OutStage<NROW> &st, int base) {
+__device__ inline void score_slot(const QRegs<DT, NROW> &Q, int32_t L, int t0, const uint8_t *slot,
+                                  OutStage<NROW> &st, int base) {
+  using S = Slot<DT, TPB>;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const int t0 = kb.t0;
+  const int col = lane & 15;
+  // row 16t + col's swizzle does not depend on the tile t
+  const int lo = S::kRowBytes * col + 16 * (g ^ swizzle<DT>(col));
+  const int hi = lo ^ 64; // chunk g + 4 (FP8)
+  auto operand = [&](int ti, v8i &b, uint32_t &bs) {
+    const uint8_t *p = slot + S::kTileBytes * ti;
+    if (DT == IDX_FP8_E4M3) {
+      b = cat(*reinterpret_cast<const v4i *>(p + lo), *reinterpret_cast<const v4i *>(p + hi));
+    } else {
+      const v4i x = *reinterpret_cast<const v4i *>(p + lo);
+      b = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+      bs = *reinterpret_cast<const uint32_t *>(slot + S::kData + 4 * (kTile * ti + col)) >> (8 * g);
+    }
+  };
+  auto mfma = [&](const v8i &b, uint32_t bs, v4f (&acc)[NROW][4]) {
+#pragma unroll
+    for (int i = 0; i < NROW; ++i) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        if (DT == IDX_FP8_E4M3)
+          acc[i][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.a[i][m], b, zero, kFmtFp8,
+                                                                       kFmtFp8, 0, 0, 0, 0);
+        else
+          acc[i][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              Q.a[i][m], b, zero, kFmtFp4, kFmtFp4, 0, Q.asc[i][m], 0, (int)bs);
+      }
+    }
+  };
   float part[NROW][TPB];
   v4f acc[2][NROW][4];
-  tile_mfma<DT, NROW, TPB>(Q, kb, 0, acc[0]);
+  v8i b[2];
+  uint32_t bs[2] = {0u, 0u};
+  operand(0, b[0], bs[0]);
+  mfma(b[0], bs[0], acc[0]);
 #pragma unroll
   for (int ti = 0; ti < TPB; ++ti) {
-    if (ti + 1 < TPB) tile_mfma<DT, NROW, TPB>(Q, kb, ti + 1, acc[(ti + 1) & 1]);
+    if (ti + 1 < TPB) {
+      operand(ti + 1, b[(ti + 1) & 1], bs[(ti + 1) & 1]);
+      mfma(b[(ti + 1) & 1], bs[(ti + 1) & 1], acc[(ti + 1) & 1]);
+    }
 #pragma unroll
     for (int i = 0; i < NROW; ++i) {
       float s = 0.f;
@@ -434,17 +475,18 @@ __device__ inline void score_block(const LogitsArgs &a, const QRegs<DT, NROW> &Q
     }
   }
   // token held by this lane after the reduction
-  const int t = TPB == 4 ? t0 + lane : t0 + 16 * (g >> 1) + (lane & 15);
+  const int tl = TPB == 4 ? lane : 16 * (g >> 1) + col;
   const bool holder = TPB == 4 || (g & 1) == 0;
-  const int tend = L - t0; // tokens of this block that the segment has
+  float ks = 1.f;
+  if (DT == IDX_FP8_E4M3) ks = *reinterpret_cast<const float *>(slot + S::kData + 4 * tl);
 #pragma unroll
   for (int i = 0; i < NROW; ++i) {
     // the head sum of w * 2 relu(s), halved (exact)
     float v = 0.5f * reduce_scatter<TPB>(part[i]);
     // the FP8 key scale of this lane's token is positive, so it commutes with
     // the ReLU and is applied once to the head sum
-    if (DT == IDX_FP8_E4M3) v *= __uint_as_float(kb.ksr);
-    if (holder && t - t0 < tend) st.v[i][t - base] = v;
+    if (DT == IDX_FP8_E4M3) v *= ks;
+    if (holder && tl < L - t0) st.v[i][t0 + tl - base] = v;
   }
 }
 
@@ -457,33 +499,99 @@ __device__ inline int32_t enter_segment(const LogitsArgs &a, int s, QRegs<DT, NR
   return L;
 }
 
-// One pipeline step: `cur` holds the loaded current block; the next block's
-// loads go into `nxt` before `cur` is scored. Returns false at the end.
-template <int DT, int NROW, int TPB>
-__device__ inline bool pipeline_step(const LogitsArgs &a, Walk &w, QRegs<DT, NROW> &Q,
-                                     int32_t &L, KBlock<TPB> &cur, KBlock<TPB> &nxt,
-                                     OutStage<NROW> &st, StageState &ss) {
-  Walk wn = w;
-  const bool more = advance(a, wn);
-  issue_block<DT, TPB>(a, wn, more, nxt);
-  if (ss.base < 0) {
-    ss.base = cur.t0 & ~(kStageTokens - 1);
-    ss.lo = cur.t0;
-  }
-  score_block<DT, NROW, TPB>(a, Q, L, cur, st, ss.base);
-  const int have = L - cur.t0; // tokens of this block that the segment has
-  ss.hi = cur.t0 + (have < a.block_tokens ? have : a.block_tokens);
-  // the next block continues this window only within the same segment
-  if (!more || wn.s != w.s || ((wn.blk * a.block_tokens) & ~(kStageTokens - 1)) != ss.base)
-    flush_stage<DT, NROW>(a, Q, st, ss);
-  if (!more) return false;
-  if (wn.s != w.s) L = enter_segment<DT, NROW>(a, wn.s, Q);
-  w = wn;
-  return true;
+// The first segment's query rows are staged through the ring's last slots:
+// per row the codes (64 heads x 128 FP8 bytes or 64 MXFP4 bytes), MXFP4's
+// E8M0 block scales (64 x 4 bytes) and the 64 fp32 weights.
+template <int DT> struct QStage {
+  static constexpr int kCodes = kHeads * (DT == IDX_FP8_E4M3 ? kHeadDim : kHeadDim / 2);
+  static constexpr int kScales = DT == IDX_FP8_E4M3 ? 0 : kHeads * (kHeadDim / 32);
+  static constexpr int kRow = kCodes + kScales + kHeads * 4;
+  static constexpr int kLoads = kCodes / 1024 + (DT == IDX_FP8_E4M3 ? 0 : 1) + 1; // per row
+};
+
+// Slots the first segment's staged queries occupy, or 0 when they take more
+// than two: those query rows are loaded into registers before the ring starts
+// (a round trip more at start-up, but an LDS ring of four slots, which keeps
+// eight work groups on a CU).
+template <int DT, int NROW, int TPB> constexpr int query_slots() {
+  constexpr int qs = (NROW * QStage<DT>::kRow + Slot<DT, TPB>::kBytes - 1) / Slot<DT, TPB>::kBytes;
+  return qs <= 2 ? qs : 0;
 }
 
+// Ring slots per work group: four (17-34 KB of LDS, so 4-8 groups share a CU).
+constexpr int kRingSlots = 4;
+
+// Issues the direct-to-LDS loads of a segment's query rows (rows[i] < 0:
+// zeros) into the staging area at lds.
+template <int DT, int NROW>
+__device__ inline void issue_query(const LogitsArgs &a, const int32_t (&rows)[NROW], uint8_t *lds) {
+  using Q = QStage<DT>;
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)lds;
+#pragma unroll
+  for (int i = 0; i < NROW; ++i) {
+    const bool live = rows[i] >= 0;
+    const int64_t r = live ? rows[i] : 0;
+    const uint32_t row = base + i * Q::kRow;
+    const v4i qr = rsrc_words(a.q + r * Q::kCodes, live ? (uint32_t)Q::kCodes : 0u);
+#pragma unroll
+    for (int j = 0; j < Q::kCodes / 1024; ++j) lds_load16(qr, row + 1024 * j, 1024 * j + 16 * lane);
+    if (DT != IDX_FP8_E4M3) {
+      const v4i sr = rsrc_words(a.q_scale + r * Q::kScales, live ? (uint32_t)Q::kScales : 0u);
+      lds_load4(sr, row + Q::kCodes, 4 * lane);
+    }
+    const v4i wr = rsrc_words(a.weights + r * kHeads, live ? (uint32_t)(kHeads * 4) : 0u);
+    lds_load4(wr, row + Q::kCodes + Q::kScales, 4 * lane);
+  }
+}
+
+// Reads staged query rows into the MFMA A operands and the lane's weights.
+template <int DT, int NROW>
+__device__ inline void read_query(QRegs<DT, NROW> &Q, const uint8_t *lds, const int32_t (&E)[NROW],
+                                  const int32_t (&out_rows)[NROW]) {
+  using S = QStage<DT>;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int hl = lane & 15;
+#pragma unroll
+  for (int i = 0; i < NROW; ++i) {
+    Q.E[i] = E[i];
+    Q.out_row[i] = out_rows[i];
+    const uint8_t *row = lds + i * S::kRow;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int h = 16 * m + hl;
+      if (DT == IDX_FP8_E4M3) {
+        const v4i *p = reinterpret_cast<const v4i *>(row + h * kHeadDim);
+        Q.a[i][m] = cat(p[g], p[4 + g]);
+      } else {
+        const v4i lo = *reinterpret_cast<const v4i *>(row + h * (kHeadDim / 2) + 16 * g);
+        Q.a[i][m] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+        Q.asc[i][m] = row[S::kCodes + h * (kHeadDim / 32) + g];
+      }
+      const v4f wv = *reinterpret_cast<const v4f *>(row + S::kCodes + S::kScales + 4 * (16 * m + 4 * g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Q.w[i][m][j] = wv[j];
+    }
+  }
+}
+
+// One wave per work group. The wave streams its range's key blocks into an
+// LDS ring with direct-to-LDS loads, R - 1 blocks ahead of the block it
+// scores: a second walk over the same range (the load walk) issues block
+// i + R - 1 into the slot block i - 1 vacated, then the wave waits until at
+// most (R - 1) blocks' loads are outstanding, which (vector-memory loads
+// complete in issue order) means block i has landed. The wave's other
+// vector-memory operations only make that wait longer, never shorter: the
+// logits stores come after the loads they could overtake, and a segment's
+// query loads are waited for in full.
 template <int DT, int NROW, int TPB>
 __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
+  using S = Slot<DT, TPB>;
+  constexpr int R = kRingSlots;
+  constexpr int QS = query_slots<DT, NROW, TPB>(); // staging slots of the first queries
+  __shared__ __attribute__((aligned(16))) uint8_t ring[R][S::kBytes];
+  __shared__ OutStage<NROW> st;
   const int c = blockIdx.x;
   Walk w;
   int32_t len0;
@@ -502,34 +610,78 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   }
   // The first block's page is read together with the segment's stored
   // length (the table entry exists whether or not the block does). The first
-  // segment's queries go out before either returns: their addresses need only
-  // the segment, so the query loads, the page lookup and then the first
-  // block's K loads overlap, with one wait for all of them.
-  const int64_t pg0 = page_of(a, w.s, (w.blk * a.block_tokens) / a.page_size);
+  // segment's queries go out (into the ring's last QS slots) before the first
+  // blocks' loads, one wait covers the queries and the first block, and the
+  // staging slots then receive the next blocks. Every load of the wave goes
+  // straight to LDS, so the compiler has no register loads of its own to wait
+  // for (such a wait would also wait for the ring).
+  int32_t pgl = block_page(a, w);
   int32_t raw0 = uniform_load(a.lens + w.s);
   w.nb = (len0 + a.block_tokens - 1) >> __builtin_ctz(a.block_tokens);
-  const bool stale = w.blk >= w.nb; // empty or stale entry
-  if (stale) {
+  if (w.blk >= w.nb) { // empty or stale entry
     if (!next_segment(a, w)) return;
     raw0 = uniform_load(a.lens + w.s);
+    pgl = block_page(a, w);
   }
   QRegs<DT, NROW> Q;
   float qs[NROW];
   int32_t L;
-  {
-    int32_t rows[NROW], E[NROW], orow[NROW];
-    L = segment_rows<NROW>(a, w.s, raw0, rows, E, orow);
-    load_query<DT, NROW, false>(Q, a, rows, E, orow, qs);
+  int32_t rows[NROW], E[NROW], orow[NROW];
+  L = segment_rows<NROW>(a, w.s, raw0, rows, E, orow);
+  Walk wl = w;      // load walk: the next block to issue, of page pgl
+  bool more_l = true;
+  int sl = 0;       // its ring slot
+  auto issue_next = [&]() {
+    issue_slot<DT, TPB>(a, wl.blk, more_l ? pgl : -1, ring[sl]);
+    sl = sl + 1 == R ? 0 : sl + 1;
+    if (more_l) {
+      more_l = advance(a, wl);
+      if (more_l) pgl = block_page(a, wl);
+    }
+  };
+  if constexpr (QS > 0) {
+#pragma unroll
+    for (int i = 0; i < NROW; ++i)
+      qs[i] = DT == IDX_FP8_E4M3 && a.q_scale != nullptr && rows[i] >= 0
+                  ? uniform_load(reinterpret_cast<const float *>(a.q_scale) + rows[i])
+                  : 1.f;
+    issue_query<DT, NROW>(a, rows, ring[R - QS]);
+#pragma unroll
+    for (int j = 0; j < R - QS; ++j) issue_next();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((R - QS - 1) * S::kLoads)); // the queries and block 0
+    read_query<DT, NROW>(Q, ring[R - QS], E, orow);
+    scale_weights(Q, qs);
+    // the staging slots are read before the next blocks' loads overwrite them
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+#pragma unroll
+    for (int j = R - QS; j < R - 1; ++j) issue_next();
+  } else {
+    load_query<DT, NROW>(Q, a, rows, E, orow, qs); // loaded and waited for
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) issue_next();
   }
-  KBlock<TPB> A, B;
-  if (!stale) issue_block_page<DT, TPB>(a, w.blk, pg0, A);
-  else issue_block<DT, TPB>(a, w, true, A);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); // the queries and the first block
-  scale_weights(Q, qs);
-  __shared__ OutStage<NROW> st;
   StageState ss;
-  while (pipeline_step<DT, NROW, TPB>(a, w, Q, L, A, B, st, ss) &&
-         pipeline_step<DT, NROW, TPB>(a, w, Q, L, B, A, st, ss)) {
+  int sc = 0; // ring slot of the block scored next
+  while (true) {
+    issue_next();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((R - 1) * S::kLoads));
+    const int t0 = w.blk * a.block_tokens;
+    if (ss.base < 0) {
+      ss.base = t0 & ~(kStageTokens - 1);
+      ss.lo = t0;
+    }
+    score_slot<DT, NROW, TPB>(Q, L, t0, ring[sc], st, ss.base);
+    sc = sc + 1 == R ? 0 : sc + 1;
+    const int have = L - t0; // tokens of this block that the segment has
+    ss.hi = t0 + (have < a.block_tokens ? have : a.block_tokens);
+    Walk wn = w;
+    const bool more = advance(a, wn);
+    // the next block continues this window only within the same segment
+    if (!more || wn.s != w.s || ((wn.blk * a.block_tokens) & ~(kStageTokens - 1)) != ss.base)
+      flush_stage<DT, NROW>(a, Q, st, ss);
+    if (!more) break;
+    if (wn.s != w.s) L = enter_segment<DT, NROW>(a, wn.s, Q);
+    w = wn;
   }
 }
 
