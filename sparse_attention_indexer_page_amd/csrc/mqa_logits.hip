@@ -331,17 +331,42 @@ __device__ inline v4i rsrc_words(const void *base, uint32_t bytes) {
 // code of the decode kernel uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm" // m0 in the clobber list
-__device__ inline void lds_load16(v4i r, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds), "v"(off),
-               "s"(r)
+__device__ inline void lds_load16(v4i r, uint32_t lds, uint32_t off, uint32_t soff = 0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds" ::"s"(lds), "v"(off),
+               "s"(r), "s"(soff)
                : "memory", "m0");
 }
-__device__ inline void lds_load4(v4i r, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen nt lds" ::"s"(lds), "v"(off),
-               "s"(r)
+__device__ inline void lds_load4(v4i r, uint32_t lds, uint32_t off, uint32_t soff = 0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen nt lds" ::"s"(lds), "v"(off),
+               "s"(r), "s"(soff)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// Lane offsets of a block's loads within its rows: unit j's chunk of row r
+// at (r * row_stride + 16 c) and the lane's scale word at (lane * scale row
+// stride). The same for every block; the block's first row comes in as the
+// instruction's scalar offset.
+template <int DT, int TPB> struct SlotOffsets {
+  uint32_t data[Slot<DT, TPB>::kDataLoads];
+  uint32_t scale;
+};
+
+template <int DT, int TPB>
+__device__ inline SlotOffsets<DT, TPB> slot_offsets(const LogitsArgs &a) {
+  using S = Slot<DT, TPB>;
+  const int lane = threadIdx.x & 63;
+  SlotOffsets<DT, TPB> o;
+#pragma unroll
+  for (int j = 0; j < S::kDataLoads; ++j) {
+    const int u = 64 * j + lane;       // 16-byte unit of the packed image
+    const int r = u / S::kUnitsPerRow; // its row
+    const int c = (u % S::kUnitsPerRow) ^ swizzle<DT>(r); // the row's chunk stored there
+    o.data[j] = (uint32_t)r * (uint32_t)a.row_stride + 16 * c;
+  }
+  o.scale = (uint32_t)lane * (uint32_t)a.scale_row_stride;
+  return o;
+}
 
 // Issues the direct-to-LDS loads of block blk (of page pg; pg < 0: none)
 // into a ring slot: always Slot::kLoads instructions, so the wave's count of
@@ -349,29 +374,25 @@ __device__ inline void lds_load4(v4i r, uint32_t lds, uint32_t off) {
 // no page the loads go through empty buffer resources: they touch no memory
 // and leave zeros. Every row of the block is loaded, also past the
 // segment's end: those rows are inside the page (or read as zeros through
-// the buffer bound) and their scores are never stored.
+// the buffer bound) and their scores are never stored. The block's first
+// row is the scalar offset: the vector offsets stay below the page's size,
+// which is all the bound checks, and the rows read lie inside the page.
 template <int DT, int TPB>
-__device__ inline void issue_slot(const LogitsArgs &a, int blk, int32_t pg, uint8_t *slot) {
+__device__ inline void issue_slot(const LogitsArgs &a, const SlotOffsets<DT, TPB> &o, int blk,
+                                  int32_t pg, uint8_t *slot) {
   using S = Slot<DT, TPB>;
-  const int lane = threadIdx.x & 63;
   const int P = a.page_size;
-  const int t0 = blk * a.block_tokens;
-  const int slot0 = t0 & (P - 1);
+  const int slot0 = (blk * a.block_tokens) & (P - 1);
   const bool valid = pg >= 0 && pg < a.num_pages;
   const int64_t p = valid ? pg : 0;
   const v4i kr = rsrc_words(a.kdata + p * a.page_stride, valid ? (uint32_t)(P * a.row_stride) : 0u);
   const v4i sr = rsrc_words(a.kscale + p * a.scale_page_stride,
                             valid ? (uint32_t)((P - 1) * a.scale_row_stride + 4) : 0u);
-  const uint32_t rs = (uint32_t)a.row_stride;
   const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)slot;
+  const uint32_t krow = (uint32_t)slot0 * (uint32_t)a.row_stride;
 #pragma unroll
-  for (int j = 0; j < S::kDataLoads; ++j) {
-    const int u = 64 * j + lane;       // 16-byte unit of the packed image
-    const int r = u / S::kUnitsPerRow; // its row
-    const int c = (u % S::kUnitsPerRow) ^ swizzle<DT>(r); // the row's chunk stored there
-    lds_load16(kr, base + 1024 * j, (uint32_t)(slot0 + r) * rs + 16 * c);
-  }
-  lds_load4(sr, base + S::kData, (uint32_t)(slot0 + lane) * (uint32_t)a.scale_row_stride);
+  for (int j = 0; j < S::kDataLoads; ++j) lds_load16(kr, base + 1024 * j, o.data[j], krow);
+  lds_load4(sr, base + S::kData, o.scale, (uint32_t)slot0 * (uint32_t)a.scale_row_stride);
 }
 
 // Logits of up to kStageTokens consecutive tokens per row (one aligned window
@@ -631,8 +652,9 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   Walk wl = w;      // load walk: the next block to issue, of page pgl
   bool more_l = true;
   int sl = 0;       // its ring slot
+  const SlotOffsets<DT, TPB> so = slot_offsets<DT, TPB>(a);
   auto issue_next = [&]() {
-    issue_slot<DT, TPB>(a, wl.blk, more_l ? pgl : -1, ring[sl]);
+    issue_slot<DT, TPB>(a, so, wl.blk, more_l ? pgl : -1, ring[sl]);
     sl = sl + 1 == R ? 0 : sl + 1;
     if (more_l) {
       more_l = advance(a, wl);
