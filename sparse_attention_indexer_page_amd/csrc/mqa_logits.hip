@@ -678,9 +678,11 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
 #pragma unroll
     for (int j = R - QS; j < R - 1; ++j) issue_next();
   } else {
-    load_query<DT, NROW>(Q, a, rows, E, orow, qs); // loaded and waited for
+    // the first blocks go out first: the query loads' full wait then also
+    // covers them, but the key stream is not held back by the query round trip
 #pragma unroll
     for (int j = 0; j < R - 1; ++j) issue_next();
+    load_query<DT, NROW>(Q, a, rows, E, orow, qs); // loaded and waited for
   }
   StageState ss;
   int sc = 0; // ring slot of the block scored next
