@@ -321,7 +321,7 @@ idx_status idx_prefill_chunked_topk(const idx_query *q, const idx_kv_cache *kv,
  * Errors: those of idx_prefill_chunked_topk; IDX_ERR_WORKSPACE when the
  * chunk plan for T and W under the capped budget needs more than the fixed
  * scratch holds (more than IDX_NOALLOC_SCHEDULE_INTS schedule entries; e.g.
- * more than about 880 thousand rows at W = 65536), checked on the host before any
+ * more than 1765888 rows at W = 65536), checked on the host before any
  * HIP call.
  */
 idx_status idx_prefill_chunked_topk_noalloc(const idx_query *q, const idx_kv_cache *kv,

@@ -122,13 +122,13 @@ int64_t prefill_chunk_rows(int32_t T, int64_t W, int64_t budget) {
   return rows < 1 ? 1 : rows;
 }
 
-// Work groups of a prefill chunk: one per block of query rows, at most 512
-// (two resident 8-wave groups per CU of an MI355X; each walks an equal share
+// Work groups of a prefill chunk: one per block of query rows, at most 256
+// (one resident 16-wave group per CU of an MI355X; each walks an equal share
 // of the chunk's key blocks).
 int32_t prefill_ctas(int64_t chunk_rows) {
   int64_t segs = (chunk_rows + idx::kPrefillRowsPerSeg - 1) / idx::kPrefillRowsPerSeg;
   if (segs < 1) segs = 1;
-  return (int32_t)(segs < 512 ? segs : 512);
+  return (int32_t)(segs < 256 ? segs : 256);
 }
 
 // Fixed device scratch of the no-allocation prefill entry: the chunk's fp32

@@ -23,12 +23,12 @@ constexpr int32_t kMaxSegLen = 1 << 22;
 __host__ __device__ inline int32_t clamp_seg_len(int32_t v) {
   return v < 0 ? 0 : (v > kMaxSegLen ? kMaxSegLen : v);
 }
-constexpr int kPrefillRowsPerSeg = 7;  // query rows sharing one K stream in prefill
-// Work-split cost of entering a segment, in key blocks. A prefill row block
-// reloads seven query rows and their lengths, a wait of about three blocks'
-// scoring time (per-group timestamps: the groups whose ranges hold many short
-// segments finished last with a cost of 1; 3 takes 1.5-2% off the longer
-// chunk of the 16384-row prefill).
+constexpr int kPrefillRowsPerSeg = 15; // query rows sharing one K stream in prefill
+// Work-split cost of entering a segment, in key blocks. Entering a prefill
+// row block, each compute wave reloads its query row with a full wait
+// (per-group timestamps of seven-row blocks: the groups whose ranges held
+// many short segments finished last at a cost of 1; 3 took 1.5-2% off the
+// longer chunk of the 16384-row prefill).
 constexpr int kPrefillEntryCost = 3;
 // A decode sequence's query rows are next_n x 8 KB of FP8, the bytes of
 // next_n x 64 key rows, loaded with a full wait when the wave enters the

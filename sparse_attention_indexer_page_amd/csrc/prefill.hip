@@ -7,14 +7,17 @@
 // see [0, visible_end) of a right-sized width, processed in Q-row chunks). Here
 // the work is a dense heads x tokens contraction per row that reuses every
 // key block across rows, so the kernel is built around key reuse:
-//   * A work group of 8 waves owns a block of 7 consecutive query rows: 7
-//     compute waves hold one row's q each (the MFMA A operands, in VGPRs), and
-//     one loader wave streams the key blocks of the schedule's item range into
-//     a 6-slot LDS ring with direct-to-LDS buffer loads; the waves score two
-//     key blocks between barriers, with two more pairs in flight. Every key block is
-//     read from L2 once per 7 rows instead of once per row. Two groups share a
-//     CU, so one group's waves fill the SIMDs while the other's wait at their
-//     stage barrier.
+//   * A work group of 16 waves (one per CU, four per SIMD) owns a block of 15
+//     consecutive query rows: 15 compute waves hold one row's q each (the MFMA
+//     A operands, in VGPRs), and one loader wave streams the key blocks of the
+//     schedule's item range into a 6-slot LDS ring with direct-to-LDS buffer
+//     loads; the waves score two key blocks between barriers, with two more
+//     pairs in flight. Every key block is read from L2 once per 15 rows.
+//     Versus two 8-wave groups of 7 rows per CU (same occupancy, same bits):
+//     the L2 -> LDS key traffic halves and the longer chunk of the 16384-row
+//     prefill takes 217.9 instead of 222-224 us on average over 23 calls, its
+//     clock-throttled peak 227 instead of 234-237 us (kernel traces, two
+//     alternating runs).
 //   * Only the loader wave issues the LDS loads and it stores nothing, so its
 //     vector-memory counter counts exactly those loads: it waits for the stage
 //     about to be consumed, then one barrier publishes it to the compute waves
@@ -256,7 +259,7 @@ __device__ inline void score_stage(const Row &R, const uint8_t *stage, int t0) {
 }
 
 template <int DT, int TPB>
-__global__ __launch_bounds__(kWaves * 64, 4) void prefill_logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(kWaves * 64, 1) void prefill_logits_kernel(LogitsArgs a) {
   using S = Stage<DT, TPB>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kStages][S::kBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave-uniform

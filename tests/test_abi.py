@@ -178,11 +178,11 @@ def test_prefill_chunk_rule_reproduces_the_pages_buffer_sizes():
     assert idx.idx_prefill_scratch_bytes(T, 4096, 256_000_000) == 4 * 4096 * 8192
     # Uneven counts: 3 chunks of at most 5 rows for 11 rows -> 4 rows each.
     assert idx.idx_prefill_scratch_bytes(11, 4096, 4 * 4096 * 5) == 4 * 4096 * 4
-    # One schedule per chunk, each for min(512, ceil(rows / 7)) work groups.
-    assert idx.idx_prefill_schedule_ints(T, 4096, 256_000_000) == 2 * idx.idx_schedule_ints(512)
+    # One schedule per chunk, each for min(256, ceil(rows / 15)) work groups.
+    assert idx.idx_prefill_schedule_ints(T, 4096, 256_000_000) == 2 * idx.idx_schedule_ints(256)
     assert idx.idx_prefill_schedule_ints(5, 4096, 1) == 5 * idx.idx_schedule_ints(1)
-    assert idx.idx_prefill_schedule_ints(T, 4096, big) == idx.idx_schedule_ints(512)
-    assert idx.idx_prefill_schedule_ints(1000, 4096, big) == idx.idx_schedule_ints(143)
+    assert idx.idx_prefill_schedule_ints(T, 4096, big) == idx.idx_schedule_ints(256)
+    assert idx.idx_prefill_schedule_ints(1000, 4096, big) == idx.idx_schedule_ints(67)
     # One row per chunk at a budget below one row.
     assert idx.idx_prefill_rows_per_chunk(4096, 1) == 1
 
@@ -378,13 +378,13 @@ def test_topk_row_loads_stay_inside_the_row(wave_kernel, NT, buckets):
 def test_prefill_noalloc_rejects_plans_beyond_its_fixed_scratch(lib):
     """The no-allocation prefill checks on the host, before any HIP call, that
     the chunk plan fits its fixed scratch: at W = 65536 the 64 MiB logits
-    cap allows 256 rows per chunk, and 1000000 rows then need 3907 schedules
-    of 37 work groups (76 entries each), more than the 2^18 entries it
-    holds."""
+    cap allows 256 rows per chunk, and 2000000 rows then need 7813 schedules
+    of 18 work groups (38 entries each), more than the 2^18 entries it
+    holds (1765888 rows fit)."""
     q, kv = _q(), _kv()
     fake = ctypes.c_void_p(0x10000)
     st = lib.idx_prefill_chunked_topk_noalloc(ctypes.byref(q), ctypes.byref(kv), fake, fake,
-                                              1000000, 65536, 1 << 40, 2048, 0, fake, None)
+                                              2000000, 65536, 1 << 40, 2048, 0, fake, None)
     assert st == idx.IDX_ERR_WORKSPACE
     assert b"fixed scratch" in lib.idx_last_error()
     for T, W, status in ((0, 4096, idx.IDX_ERR_INVALID), (10, 0, idx.IDX_ERR_INVALID),

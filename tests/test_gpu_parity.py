@@ -329,13 +329,13 @@ def test_prefill_small_matches_oracle_and_is_chunk_invariant(dtype, P):
     lg = scratch.numpy().reshape(case.T, case.W)
     for r in rows:
         # rows seeing at most k keys select them all: their scores are only
-        # computed when a longer row shares their block of seven rows
+        # computed when a longer row shares their block of fifteen rows
         if E[r] > case.k:
             check_logits(lg[r], ref[r], E[r], "prefill row %d" % r)
         check_topk_band(out[r].numpy(), ref[r], E[r], case.k, "prefill row %d" % r)
-    # the first two row blocks (rows 0-13, at most 28 <= k keys each) are not
-    # scored at all: their scratch rows keep the NaN fill
-    assert np.all(np.isnan(lg[:14]))
+    # the first row block (rows 0-14, at most 30 <= k keys each) is not
+    # scored at all: its scratch rows keep the NaN fill
+    assert np.all(np.isnan(lg[:15]))
     for budget in (4 * case.W * 100, 4 * case.W * 7, 4 * case.W, 1):
         _, o2 = run_prefill(dc, budget=budget)
         assert torch.equal(o2, out), "budget %d changed the selection" % budget
