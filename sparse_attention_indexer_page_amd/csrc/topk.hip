@@ -154,6 +154,10 @@ struct TopkShared {
 
 // Histogram of digit(key) over the keys accepted by `in`, then the bin that
 // holds the need-th largest: returns (bin, count above it, count in it).
+// The histogram is all zero on entry (cleared at the start of the row, and
+// each pass clears the bins it reads), so a pass takes three barriers: the
+// first also orders every earlier read of red and sel before this pass
+// writes them.
 template <int NT, typename Visit>
 __device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit, uint32_t &bin,
                                   int &above, int &inbin) {
@@ -162,20 +166,18 @@ __device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  __syncthreads(); // every thread is done reading red/sel/hist of the last step
-#pragma unroll
-  for (int q = 0; q < BPT; ++q) sm.hist[tid * BPT + q] = 0;
-  __syncthreads();
   visit([&](uint32_t d) { atomicAdd(&sm.hist[d], 1u); });
   __syncthreads();
   // Block-wide scan from the highest bin down: thread t owns bins
-  // [kBins-1-t*BPT, kBins-1-(t+1)*BPT).
+  // [kBins-1-t*BPT, kBins-1-(t+1)*BPT), and clears them for the next pass
+  // (whose first add follows this pass's last barrier).
   const int top = kBins - 1 - tid * BPT;
   uint32_t cnt[BPT];
   uint32_t mine = 0;
 #pragma unroll
   for (int q = 0; q < BPT; ++q) {
     cnt[q] = sm.hist[top - q];
+    sm.hist[top - q] = 0u;
     mine += cnt[q];
   }
   const uint32_t incl = wave_incl_scan_u32(mine);
@@ -204,7 +206,8 @@ __device__ __forceinline__ void radix_pass(TopkShared &sm, int need, Visit visit
 }
 
 // Block-wide max and min of per-thread values and sum of per-wave counts
-// (wave-uniform `cnt`); uniform results.
+// (wave-uniform `cnt`); uniform results. The first use of red in the work
+// group: nothing has read it before.
 template <int NT>
 __device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint32_t &mn,
                                               uint32_t &cnt) {
@@ -213,7 +216,6 @@ __device__ __forceinline__ void block_max_min(TopkShared &sm, uint32_t &mx, uint
   const int wave = threadIdx.x >> 6;
   mx = wave_max_u32(mx);
   mn = wave_min_u32(mn);
-  __syncthreads(); // red is free
   if (lane == 0) {
     sm.red[wave] = mx;
     sm.red[16 + wave] = mn;
@@ -330,6 +332,10 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
     sm.ncand = 0;
     sm.nsmall = 0;
   }
+  // the histogram starts zeroed (ordered before the first pass by the
+  // barrier of block_max_min)
+#pragma unroll
+  for (int q = 0; q < kBins / NT; ++q) sm.hist[tid * (kBins / NT) + q] = 0u;
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
