@@ -302,6 +302,114 @@ __device__ __forceinline__ void emit_selection(TopkShared &sm, KeyAt key_at, Idx
   }
 }
 
+// The exact selection over candidates compacted into LDS in index order:
+// sm.cand[0, nc) with their row indices in sm.cidx (complete since a barrier
+// before the call), every key of the row >= lo among them, hi the largest;
+// k <= nc of them are taken. Refines by key bits within [lo, hi] (radix
+// passes over the LDS candidates, then one wave ranks the last few) and
+// writes the selection in index order.
+template <int NT>
+__device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_t lo, uint32_t hi,
+                                                 int k, int32_t ib, int32_t *out) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int need = k, cand = nc;
+  uint32_t thr;    // final rule: key > thr, plus need_eq keys == thr (lowest index first)
+  int need_eq = 0; // 0: every key >= thr + 1 is taken
+  int n_eq_total = -1;
+  while (true) {
+    if (lo == hi) { // a single key value
+      thr = lo;
+      need_eq = need;
+      n_eq_total = cand;
+      break;
+    }
+    if (cand <= kRankCap) {
+      // one wave ranks the candidates: lane l holds candidate l
+      const bool direct = cand == nc; // every compacted key is a candidate
+      if (!direct) {
+        for (int c0 = wave * 64; c0 < nc; c0 += NT) {
+          const int c = c0 + lane;
+          const uint32_t x = c < nc ? sm.cand[c] : 0u;
+          const bool in = c < nc && x >= lo && x <= hi;
+          const uint64_t m = __ballot(in);
+          if (m) {
+            uint32_t at = 0;
+            if (lane == 0) at = atomicAdd(&sm.nsmall, (uint32_t)__popcll(m));
+            at = __builtin_amdgcn_readlane(at, 0);
+            if (in) sm.small[at + lanes_below(m)] = x;
+          }
+        }
+        __syncthreads();
+      }
+      if (wave == 0) {
+        const uint32_t *src = direct ? sm.cand : sm.small;
+        const uint32_t mykey = lane < cand ? src[lane] : 0u;
+        int gt = 0, eq = 0;
+        for (int j = 0; j < cand; ++j) {
+          const uint32_t x = __builtin_amdgcn_readlane(mykey, j);
+          gt += x > mykey ? 1 : 0;
+          eq += x == mykey ? 1 : 0;
+        }
+        const bool is_thr = lane < cand && gt < need && gt + eq >= need;
+        const int tl = (int)__builtin_ctzll(__ballot(is_thr));
+        if (lane == tl) {
+          sm.sel[0] = mykey;
+          sm.sel[1] = (uint32_t)(need - gt);
+          sm.sel[2] = (uint32_t)eq;
+        }
+      }
+      __syncthreads();
+      thr = sm.sel[0];
+      need_eq = (int)sm.sel[1];
+      n_eq_total = (int)sm.sel[2];
+      break;
+    }
+    const uint32_t range = hi - lo;
+    const int bits = 32 - __builtin_clz(range);
+    const int shift = bits > kDigitBits ? bits - kDigitBits : 0;
+    uint32_t bin;
+    int above, inbin;
+    radix_pass<NT>(
+        sm, need,
+        [&](auto add) {
+          for (int c = tid; c < nc; c += NT) {
+            const uint32_t x = sm.cand[c];
+            if (x >= lo && x <= hi) add((x - lo) >> shift);
+          }
+        },
+        bin, above, inbin);
+    need -= above;
+    cand = inbin;
+    const uint32_t nlo = lo + (bin << shift);
+    const uint32_t width = (1u << shift) - 1u;
+    hi = hi - nlo < width ? hi : nlo + width;
+    lo = nlo;
+    if (inbin == need) { // the whole bin is taken
+      thr = lo - 1u;
+      break;
+    }
+  }
+  // every key equal to thr is taken: the rule is key >= thr_ge
+  const bool all_ties = need_eq == 0 || need_eq == n_eq_total;
+  const uint32_t thr_ge = need_eq == 0 ? thr + 1u : thr;
+  // over the compacted keys: wave w owns entries [w * run, w * run + run)
+  constexpr int NQ = kCandCap / NT; // runs of 64 per wave (run <= kCandCap / NW)
+  static_assert(kCandCap % NT == 0, "whole runs per wave");
+  const int run = (((nc + NW - 1) / NW) + 63) & ~63;
+  const int j0 = wave * run + lane;
+  emit_selection<NT, NQ>(
+      sm,
+      [&](int q) -> uint32_t {
+        const int j = j0 + 64 * q;
+        return 64 * q < run && j < nc ? sm.cand[j] : 0u;
+      },
+      [&](int q) -> int32_t { return ib + (int32_t)sm.cidx[j0 + 64 * q]; }, thr, need_eq, all_ties,
+      thr_ge, k, out);
+}
+
 // Selects the top k of a row of E > k scores, IPT keys per lane.
 template <int NT, int IPT>
 __device__ __forceinline__ void select_row(const float *row, int E, int k, int32_t *out,
@@ -360,8 +468,7 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   int need_eq = 0; // 0: every key >= thr + 1 is taken
   int n_eq_total = -1;
   bool done = false;
-  bool in_lds = false;    // the candidates are sm.cand[0, nc)
-  bool compacted = false; // ... and they are every key >= lo, in index order (sm.cidx)
+  bool in_lds = false; // the candidates are sm.cand[0, nc)
   int nc = 0;
 
   // Bins by value, linear between the row's extremes (a monotone map: a
@@ -420,16 +527,13 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
         at += (uint32_t)__popcll(mk);
       }
       __syncthreads();
-      compacted = true;
-      in_lds = true;
-      nc = (int)total;
-      cand = (int)total;
-      lo = thr0;
+      select_compacted<NT>(sm, (int)total, thr0, kmax, k, ib, out);
+      return;
     }
   }
 
   // ---- pass 1 over every key, by value bin
-  if (linear && !compacted) {
+  if (linear) {
     uint32_t bin;
     int above, inbin;
     radix_pass<NT>(
@@ -588,26 +692,10 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   const bool all_ties = need_eq == 0 || need_eq == n_eq_total;
   const uint32_t thr_ge = need_eq == 0 ? thr + 1u : thr;
 
-  if (compacted) {
-    // over the compacted keys: wave w owns entries [w * run, w * run + run)
-    constexpr int NQ = kCandCap / NT; // runs of 64 per wave (run <= kCandCap / NW)
-    static_assert(kCandCap % NT == 0, "whole runs per wave");
-    const int run = (((nc + NW - 1) / NW) + 63) & ~63;
-    const int j0 = wave * run + lane;
-    emit_selection<NT, NQ>(
-        sm,
-        [&](int q) -> uint32_t {
-          const int j = j0 + 64 * q;
-          return 64 * q < run && j < nc ? sm.cand[j] : 0u;
-        },
-        [&](int q) -> int32_t { return ib + (int32_t)sm.cidx[j0 + 64 * q]; }, thr, need_eq,
-        all_ties, thr_ge, k, out);
-  } else {
-    emit_selection<NT, IPT>(
-        sm, [&](int i) -> uint32_t { return key[i]; },
-        [&](int i) -> int32_t { return ib + base + i * 64 + lane; }, thr, need_eq, all_ties,
-        thr_ge, k, out);
-  }
+  emit_selection<NT, IPT>(
+      sm, [&](int i) -> uint32_t { return key[i]; },
+      [&](int i) -> int32_t { return ib + base + i * 64 + lane; }, thr, need_eq, all_ties, thr_ge,
+      k, out);
 }
 
 template <int NT, int MAXIPT>
@@ -641,6 +729,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     select_row<NT, (MAXIPT >= 32 ? 32 : 4)>(row, E, k, out, ib, sm);
   else if (MAXIPT >= 64) select_row<NT, (MAXIPT >= 64 ? 64 : 4)>(row, E, k, out, ib, sm);
 }
+
 
 // ---- one wave per row, for widths up to 4096 --------------------------------
 //
