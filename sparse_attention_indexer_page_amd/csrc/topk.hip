@@ -421,21 +421,29 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   const int rounds = (E + NW * 64 - 1) / (NW * 64); // <= IPT
   const int base = wave * rounds * 64;               // wave's first index
 
-  // ---- keys (0 past the row: every visible key is > 0x007FFFFF)
-  uint32_t key[IPT];
   // Loads through a buffer resource bounded by the row's E scores: past the
   // row they return 0 without a predicate and touch no memory; such items
-  // then get key 0. The item step is part of the vector offset, which the
-  // hardware checks against the bound (the scalar offset is not checked).
+  // then get key 0 (every visible key is > 0x007FFFFF). The item step is part
+  // of the vector offset, which the hardware checks against the bound (the
+  // scalar offset is not checked).
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(row), (short)0, E * 4, 0x00020000);
+  // ---- the sample for the threshold estimate goes out first: 16 consecutive
+  // scores out of every 256 (a sixteenth of the row's bytes), so that the
+  // estimate runs while the row's own loads are still arriving (one CU pulls
+  // a row at ~28 GB/s: ~5 us for 32K scores).
+  constexpr int SPT = (IPT + 15) / 16; // sampled scores per lane (E <= IPT * NT)
+  uint32_t sbits[SPT];
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int q = tid + NT * u;
+    sbits[u] = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)((q >> 4) * 256 + (q & 15)) * 4u, 0, 0);
+  }
+  uint32_t key[IPT]; // the row's raw bits, keys once the estimate is made
   const uint32_t voff = (uint32_t)(base + lane) * 4u;
   const int left = E - base - lane; // item i is visible iff 64 * i < left
 #pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rr, voff + 256u * i, 0, 0);
-    key[i] = (i < rounds && 64 * i < left) ? float_key(__uint_as_float(bits)) : 0u;
-  }
+  for (int i = 0; i < IPT; ++i) key[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, voff + 256u * i, 0, 0);
   if (tid == 0) {
     sm.ncand = 0;
     sm.nsmall = 0;
@@ -444,7 +452,99 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   // barrier of block_max_min)
 #pragma unroll
   for (int q = 0; q < kBins / NT; ++q) sm.hist[tid * (kBins / NT) + q] = 0u;
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+
+  // ---- sampled threshold: the lower edge thr0 of the value bin (linear
+  // between the sample's extremes) that holds the m-th largest of the n_smp
+  // sampled keys, m chosen so that about min(2k, (k + kCandCap) / 2) of the
+  // row's keys lie at or above it. When between k and kCandCap of them do
+  // (counted exactly), those keys and their indices are compacted into LDS
+  // in index order, and the exact selection and the output run over them
+  // alone. Otherwise the estimate is dropped (nothing is decided by it) and
+  // the full passes over the row follow.
+  const bool sampled = E > kCandCap && 2 * k <= kCandCap;
+  uint32_t thr0 = 0u;
+  bool estimated = false;
+  if (sampled) {
+    uint32_t smp[SPT], smax = 0u, smin = 0xFFFFFFFFu, n_smp = 0u;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int q = tid + NT * u;
+      smp[u] = (q >> 4) * 256 + (q & 15) < E ? float_key(__uint_as_float(sbits[u])) : 0u;
+      if (smp[u] != 0u) {
+        smax = smp[u] > smax ? smp[u] : smax;
+        smin = smp[u] < smin ? smp[u] : smin;
+      }
+      n_smp += (uint32_t)__popcll(__ballot(smp[u] != 0u));
+    }
+    block_max_min<NT>(sm, smax, smin, n_smp); // n_smp > 0: position 0 is sampled
+    const float h0 = key_float(smin) * 0.5f;
+    const float hr = key_float(smax) * 0.5f - h0;
+    const float scale = (float)kBins / hr;
+    if (hr > 0.f && scale < 3.0e38f) {
+      auto vbin = [&](uint32_t kk) -> uint32_t {
+        const float x = __builtin_fmaf(key_float(kk), 0.5f, -h0) * scale;
+        return (uint32_t)fminf(x, (float)(kBins - 1));
+      };
+      const int target = (k + kCandCap) / 2 < 2 * k ? (k + kCandCap) / 2 : 2 * k;
+      const int64_t mm = ((int64_t)n_smp * target + E - 1) / E;
+      const int m = mm < 1 ? 1 : (mm > (int64_t)n_smp ? (int)n_smp : (int)mm);
+      uint32_t b0;
+      int a0, i0;
+      radix_pass<NT>(
+          sm, m,
+          [&](auto add) {
+#pragma unroll
+            for (int u = 0; u < SPT; ++u)
+              if (smp[u] != 0u) add(vbin(smp[u]));
+          },
+          b0, a0, i0);
+      thr0 = first_key_in_bin_near(smin - 1u, smax, b0, bin_edge_key(b0, h0, scale), vbin);
+      estimated = true;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IPT; ++i)
+    key[i] = (i < rounds && 64 * i < left) ? float_key(__uint_as_float(key[i])) : 0u;
+  if (estimated) {
+    uint32_t n0 = 0; // this wave's keys >= thr0 (key 0, past the row, is below thr0)
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) n0 += (uint32_t)__popcll(__ballot(key[i] >= thr0));
+    // red was last read (block_max_min) before radix_pass's barriers
+    if (lane == 0) sm.red[wave] = n0;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? sm.red[w] : 0u;
+      total += sm.red[w];
+    }
+    if (total >= (uint32_t)k && total <= (uint32_t)kCandCap) {
+      uint32_t at = before, mx = 0u;
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const bool c = key[i] >= thr0;
+        const uint64_t mk = __ballot(c);
+        if (c) {
+          const uint32_t q = at + (uint32_t)lanes_below(mk);
+          sm.cand[q] = key[i];
+          sm.cidx[q] = (uint32_t)(base + 64 * i + lane);
+        }
+        at += (uint32_t)__popcll(mk);
+        mx = key[i] > mx ? key[i] : mx; // the row's largest key is a candidate
+      }
+      mx = wave_max_u32(mx);
+      if (lane == 0) sm.red[16 + wave] = mx; // red[0, NW) is still being read
+      __syncthreads();
+      mx = 0u;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mx = sm.red[16 + w] > mx ? sm.red[16 + w] : mx;
+      select_compacted<NT>(sm, (int)total, thr0, mx, k, ib, out);
+      return;
+    }
+  }
+
+  // ---- the row's extremes, for the full passes
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, unused = 0u;
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     if (key[i] != 0u) {
@@ -452,14 +552,8 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
       kmin = key[i] < kmin ? key[i] : kmin;
     }
   }
-  // One sampled key per thread, spread over the wave's run of the row (item
-  // lane % rounds of each lane), for the threshold estimate below.
-  const int si = lane % rounds;
-  uint32_t smp = 0u;
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) smp = i == si ? key[i] : smp;
-  uint32_t n_smp = (uint32_t)__popcll(__ballot(smp != 0u));
-  block_max_min<NT>(sm, kmax, kmin, n_smp);
+  if (sampled) __syncthreads(); // red was read above
+  block_max_min<NT>(sm, kmax, kmin, unused);
 
   // The candidates are the keys in [lo, hi]; `need` of them remain to take.
   uint32_t lo = kmin, hi = kmax;
@@ -482,55 +576,6 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
     const float x = __builtin_fmaf(key_float(kk), 0.5f, -h0) * scale;
     return (uint32_t)fminf(x, (float)(kBins - 1));
   };
-
-  // ---- sampled threshold: the lower edge thr0 of the value bin that holds
-  // the m-th largest of the n_smp sampled keys, m chosen so that about
-  // min(2k, (k + kCandCap) / 2) of the row's keys lie at or above it. When
-  // between k and kCandCap of them do (counted exactly), those keys and their
-  // indices are compacted into LDS in index order, and the exact selection
-  // and the output run over them alone: two passes over the row instead of
-  // the four below. Otherwise the estimate is dropped (nothing is decided by
-  // it) and the full passes follow.
-  if (linear && E > kCandCap && 2 * k <= kCandCap && n_smp > 0u) {
-    const int target = (k + kCandCap) / 2 < 2 * k ? (k + kCandCap) / 2 : 2 * k;
-    const int64_t mm = ((int64_t)n_smp * target + E - 1) / E;
-    const int m = mm < 1 ? 1 : (mm > (int64_t)n_smp ? (int)n_smp : (int)mm);
-    uint32_t b0;
-    int a0, i0;
-    radix_pass<NT>(
-        sm, m, [&](auto add) { if (smp != 0u) add(vbin(smp)); }, b0, a0, i0);
-    const uint32_t thr0 =
-        first_key_in_bin_near(kmin - 1u, kmax, b0, bin_edge_key(b0, h0, scale), vbin);
-    uint32_t n0 = 0; // this wave's keys >= thr0 (key 0, past the row, is below thr0)
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) n0 += (uint32_t)__popcll(__ballot(key[i] >= thr0));
-    // red was last read before radix_pass's final barrier
-    if (lane == 0) sm.red[wave] = n0;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      before += w < wave ? sm.red[w] : 0u;
-      total += sm.red[w];
-    }
-    if (total >= (uint32_t)k && total <= (uint32_t)kCandCap) {
-      uint32_t at = before;
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        const bool c = key[i] >= thr0;
-        const uint64_t mk = __ballot(c);
-        if (c) {
-          const uint32_t q = at + (uint32_t)lanes_below(mk);
-          sm.cand[q] = key[i];
-          sm.cidx[q] = (uint32_t)(base + 64 * i + lane);
-        }
-        at += (uint32_t)__popcll(mk);
-      }
-      __syncthreads();
-      select_compacted<NT>(sm, (int)total, thr0, kmax, k, ib, out);
-      return;
-    }
-  }
 
   // ---- pass 1 over every key, by value bin
   if (linear) {

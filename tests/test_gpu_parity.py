@@ -246,16 +246,11 @@ def test_topk_wave_kernel_adversarial_rows_exact(k):
         check_topk_exact(o[r], vals[r], int(E[r]), k, "k=%d row %d (E=%d)" % (k, r, E[r]))
 
 
-def _sampled_positions(E, NT=1024):
-    """Row positions whose keys the wide-row selection samples for its
-    threshold estimate: wave w of the NT / 64 waves owns the run
-    [w * rounds * 64, ...), rounds = ceil(E / NT), and lane l samples item
-    l % rounds of that run."""
-    rounds = -(-E // NT)
-    w = np.arange(NT // 64)[:, None]
-    lane = np.arange(64)[None, :]
-    p = (w * rounds * 64 + 64 * (lane % rounds) + lane).ravel()
-    return p[p < E]
+def _sampled_positions(E):
+    """Row positions whose scores the wide-row selection samples for its
+    threshold estimate: the first 16 of every 256."""
+    p = np.arange(E)
+    return p[(p % 256) < 16]
 
 
 @pytest.mark.parametrize("k", [64, 700, 2048])
