@@ -122,9 +122,11 @@ int32_t idx_recommended_ctas(int32_t rows);
  * 64-token blocks (pages of 64 or 256 rows) with one query row per sequence
  * stream 8 KB blocks, and one wave per SIMD (4 per CU) keeps enough of them
  * in flight while no two waves of a SIMD compete for issue; smaller blocks
- * (32-row pages, MXFP4 keys) or several query rows per sequence want two
- * waves per SIMD (8 per CU). At least `rows`. Host only; 0 when no device
- * is present or dtype / page_size / next_n are not supported values. */
+ * (32-row pages, MXFP4 keys) want two waves per SIMD (8 per CU) where the
+ * CU's 160 KB of LDS holds eight of their work groups (up to three query rows
+ * per sequence), else 4 per CU, so every work group is resident at once. At
+ * least `rows`. Host only; 0 when no device is present or dtype / page_size /
+ * next_n are not supported values. */
 int32_t idx_recommended_decode_ctas(int32_t rows, int32_t dtype, int32_t page_size,
                                     int32_t next_n);
 

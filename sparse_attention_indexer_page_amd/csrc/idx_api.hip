@@ -235,9 +235,12 @@ int32_t idx_recommended_decode_ctas(int32_t rows, int32_t dtype, int32_t page_si
   // batched decode, FP8, 64-row pages: 1024 work groups 29.8 us, 768: 30.7,
   // 1536: 35.6, 2048: 34.7 (four 8.4 KB ring slots per group: four groups
   // per CU); MTP (32-row pages, two rows) and MXFP4 (4.3 KB slots, eight
-  // groups per CU): 2048 beat 1024 by 10% and 7%
+  // groups per CU): 2048 beat 1024 by 10% and 7%. Two groups per SIMD where
+  // the LDS holds eight groups, else one: every group is resident at once.
+  const int lds = idx::decode_lds_bytes(dtype == IDX_FP8_E4M3, idx::block_tokens(page_size), next_n);
   const bool big_blocks = dtype == IDX_FP8_E4M3 && idx::block_tokens(page_size) == 64 && next_n == 1;
-  int64_t n = (int64_t)cus * (big_blocks ? 4 : 8);
+  const int per_cu = !big_blocks && 8 * lds <= idx::kLdsBytesPerCu ? 8 : 4;
+  int64_t n = (int64_t)cus * per_cu;
   if (rows > n) n = rows;
   return (int32_t)(n < kMaxCtas ? n : kMaxCtas);
 }

@@ -44,6 +44,16 @@ __host__ __device__ inline int decode_entry_cost(int next_n, int block_tokens) {
 // Tokens per schedule block: a block never straddles two pages.
 inline int block_tokens(int page_size) { return page_size < 64 ? page_size : 64; }
 
+// LDS of one decode scoring work group: a ring of four slots, each a block's
+// key rows (128 B FP8, 64 B MXFP4 per token) and 256 B of scale words, plus
+// the 1 KB output stage of each query row. The kernel checks its own size
+// against this; the work-group count the library recommends follows from it.
+__host__ __device__ constexpr int decode_ring_slots() { return 4; }
+__host__ __device__ constexpr int decode_lds_bytes(bool fp8, int block_tokens, int next_n) {
+  return decode_ring_slots() * ((fp8 ? 128 : 64) * block_tokens + 256) + next_n * 1024;
+}
+constexpr int kLdsBytesPerCu = 160 * 1024;
+
 enum SegMode : int {
   kSegDecode = 0,  // segment = sequence; length = context_lens[s]
   kSegPrefill = 1, // segment = kPrefillRowsPerSeg consecutive query rows;

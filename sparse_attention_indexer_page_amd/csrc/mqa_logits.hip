@@ -540,7 +540,7 @@ template <int DT, int NROW, int TPB> constexpr int query_slots() {
 }
 
 // Ring slots per work group: four (17-34 KB of LDS, so 4-8 groups share a CU).
-constexpr int kRingSlots = 4;
+constexpr int kRingSlots = decode_ring_slots();
 
 // Issues the direct-to-LDS loads of a segment's query rows (rows[i] < 0:
 // zeros) into the staging area at lds.
@@ -613,6 +613,9 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   constexpr int QS = query_slots<DT, NROW, TPB>(); // staging slots of the first queries
   __shared__ __attribute__((aligned(16))) uint8_t ring[R][S::kBytes];
   __shared__ OutStage<NROW> st;
+  static_assert(sizeof(ring) + sizeof(st) ==
+                    decode_lds_bytes(DT == IDX_FP8_E4M3, TPB * kTile, NROW),
+                "the recommended work-group count assumes this LDS size");
   const int c = blockIdx.x;
   Walk w;
   int32_t len0;

@@ -90,13 +90,16 @@ def _bench_ctas(case):
 
 
 def test_recommended_decode_work_groups():
-    """4 per CU for FP8 keys in 64-token blocks with one row per sequence,
-    8 per CU otherwise, at least the row count; 0 for unsupported values."""
+    """4 per CU for FP8 keys in 64-token blocks, 8 per CU for smaller blocks
+    where eight work groups' LDS fits a CU (up to three rows per sequence),
+    else 4; at least the row count; 0 for unsupported values."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert idx.idx_recommended_decode_ctas(64, synth.FP8, 64, 1) == 4 * cus
     assert idx.idx_recommended_decode_ctas(64, synth.FP8, 256, 1) == 4 * cus
     assert idx.idx_recommended_decode_ctas(64, synth.FP8, 32, 1) == 8 * cus
-    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 64, 2) == 8 * cus
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 64, 2) == 4 * cus  # 35 KB of LDS each
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 32, 3) == 8 * cus  # 20 KB: eight fit
+    assert idx.idx_recommended_decode_ctas(64, synth.FP8, 32, 4) == 4 * cus  # 21 KB: seven would
     assert idx.idx_recommended_decode_ctas(64, synth.MXFP4, 256, 1) == 8 * cus
     assert idx.idx_recommended_decode_ctas(100000, synth.FP8, 64, 1) == 100000
     assert idx.idx_recommended_decode_ctas(64, 7, 64, 1) == 0
