@@ -1,6 +1,7 @@
 // C ABI of the indexer library: host-side validation and kernel dispatch.
 // Every check here runs before any HIP call, so a rejected call leaves the
 // device untouched; nothing here allocates, frees or synchronizes.
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <stdarg.h>
@@ -81,6 +82,23 @@ idx_status check_cache(const idx_kv_cache *kv, int32_t dtype) {
   if ((int64_t)kv->page_size * kv->scale_row_stride_bytes >= (1ll << 31))
     return fail(IDX_ERR_INVALID, "scale page extent must stay below 2 GiB");
   return IDX_OK;
+}
+
+// Compute units of the current device, looked up once per device (0 when
+// none is present).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 idx::LogitsArgs logits_args(const idx_query *q, const idx_kv_cache *kv) {
@@ -309,6 +327,8 @@ idx_status decode_logits(const idx_query *q, const idx_kv_cache *kv, const int32
   a.row_cap = B * next_n;
   a.cta_info = cta_info;
   a.n_ctas = n_ctas;
+  const int cus = device_cus();
+  a.lead_ctas = !cta_info && cus > 0 && cus <= 1024 && n_ctas == 8 * cus ? 4 * cus : 0;
   a.logits = logits;
   a.W = W;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -110,6 +110,9 @@ struct LogitsArgs {
                                // keys is not scored (its top-k is every visible key)
   const int32_t *cta_info;
   int32_t n_ctas;
+  int32_t lead_ctas; // decode without cta_info: when the launch holds two work groups per SIMD,
+                     // the first lead_ctas (dispatched first, one per SIMD) take 4/3 of a
+                     // share each; 0: equal shares
   // output
   float *logits; // decode [B*next_n][W]; prefill [row_end-row0][W]
   int64_t W;

@@ -213,7 +213,12 @@ __device__ inline int32_t wave_incl_scan(int32_t v) {
 // (same costs: ceil(len / BK) blocks per non-empty sequence plus the decode
 // entry cost; range c starts at unit floor(c * N / n_ctas) of the N units),
 // from all B <= kInlineSplitMaxSegs lengths at once, 64 sequences per lane
-// slot.
+// slot. With two work groups per SIMD (lead_ctas > 0) the shares are
+// weighted instead: the first lead_ctas groups, dispatched first and one per
+// SIMD, win issue arbitration over the second group on their SIMD and take
+// 4/3 of a share each (range c starts at floor(cum(c) * N / cum(n_ctas)),
+// cum(c) = 4 min(c, lead) + 3 max(c - lead, 0); MXFP4 decode 65.0 -> 63.7 us,
+// MTP 42.1 -> 41.1 us, over a four-copy pool rotation, two runs each).
 __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   constexpr int kChunks = kInlineSplitMaxSegs / 64;
   const int lane = threadIdx.x & 63;
@@ -239,11 +244,19 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
   int32_t len0 = 0; // length of the range's first sequence
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    // floor((c + e) N / n_ctas) through one double division: the numerator
-    // (< 2^51) and n_ctas (<= 2^20) are exact, and a non-integer quotient
-    // (< 2^31) lies at least 1/n_ctas from an integer, far beyond the
-    // division's rounding error (< 2^-22), so truncation gives the floor
-    const int64_t T = (int64_t)((double)((int64_t)(c + e) * N) / (double)a.n_ctas);
+    // floor(cum(c + e) N / cum(n_ctas)) through one double division: the
+    // numerator (< 2^51; weighted, lead_ctas <= 2^12: < 2^46) and the
+    // denominator (<= 2^20) are exact, and a non-integer quotient (< 2^31)
+    // lies at least 1/denominator from an integer, far beyond the division's
+    // rounding error (< 2^-22), so truncation gives the floor
+    const int64_t ce = c + e;
+    int64_t num = ce, den = a.n_ctas;
+    if (a.lead_ctas > 0) {
+      const int64_t lead = a.lead_ctas;
+      num = 4 * (ce < lead ? ce : lead) + 3 * (ce > lead ? ce - lead : 0);
+      den = 4 * lead + 3 * (a.n_ctas - lead);
+    }
+    const int64_t T = (int64_t)((double)(num * N) / (double)den);
     int32_t seg = a.nseg, blk = 0;
     if (T < N) {
       // the last sequence whose prefix is <= T holds unit T
