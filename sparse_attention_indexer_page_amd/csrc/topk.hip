@@ -273,7 +273,10 @@ __device__ __forceinline__ void emit_selection(TopkShared &sm, KeyAt key_at, Idx
     eq_before += w < wave ? (int)sm.red[16 + w] : 0;
   }
 
-  // ---- writing pass in index order
+  // ---- writing pass in index order (the comparisons are made again rather
+  // than kept from the counting pass: 2 N ballots held across its barriers
+  // would not fit the scalar registers)
+  asm volatile("" : "+v"(thr), "+v"(thr_ge));
   if (all_ties) {
     int pos = gt_before;
 #pragma unroll
@@ -303,11 +306,14 @@ __device__ __forceinline__ void emit_selection(TopkShared &sm, KeyAt key_at, Idx
 }
 
 // The exact selection over candidates compacted into LDS in index order:
-// sm.cand[0, nc) with their row indices in sm.cidx (complete since a barrier
-// before the call), every key of the row >= lo among them, hi the largest;
-// k <= nc of them are taken. Refines by key bits within [lo, hi] (radix
-// passes over the LDS candidates, then one wave ranks the last few) and
-// writes the selection in index order.
+// sm.cand[0, nc) holds their raw score bits (keyed here, as they are read)
+// and sm.cidx their row indices (both complete since a barrier before the
+// call); every key of the row >= lo is among them; k <= nc of them are taken.
+// hi >= lo is a key of the row (the largest of a sample): the first pass bins
+// [lo, hi] by key bits and puts every key beyond its top bin into that bin,
+// so the bins stay key intervals (the top one open above). Refines by key
+// bits within the chosen interval (radix passes over the LDS candidates, then
+// one wave ranks the last few) and writes the selection in index order.
 template <int NT>
 __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_t lo, uint32_t hi,
                                                  int k, int32_t ib, int32_t *out) {
@@ -319,20 +325,22 @@ __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_
   uint32_t thr;    // final rule: key > thr, plus need_eq keys == thr (lowest index first)
   int need_eq = 0; // 0: every key >= thr + 1 is taken
   int n_eq_total = -1;
+  bool open = true; // keys above hi may remain (first pass only)
   while (true) {
-    if (lo == hi) { // a single key value
+    if (!open && lo == hi) { // a single key value
       thr = lo;
       need_eq = need;
       n_eq_total = cand;
       break;
     }
     if (cand <= kRankCap) {
-      // one wave ranks the candidates: lane l holds candidate l
+      // one wave ranks the candidates: lane l holds candidate l (on the first
+      // pass every compacted key is one, so hi is not used)
       const bool direct = cand == nc; // every compacted key is a candidate
       if (!direct) {
         for (int c0 = wave * 64; c0 < nc; c0 += NT) {
           const int c = c0 + lane;
-          const uint32_t x = c < nc ? sm.cand[c] : 0u;
+          const uint32_t x = c < nc ? float_key(__uint_as_float(sm.cand[c])) : 0u;
           const bool in = c < nc && x >= lo && x <= hi;
           const uint64_t m = __ballot(in);
           if (m) {
@@ -345,8 +353,8 @@ __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_
         __syncthreads();
       }
       if (wave == 0) {
-        const uint32_t *src = direct ? sm.cand : sm.small;
-        const uint32_t mykey = lane < cand ? src[lane] : 0u;
+        const uint32_t mykey =
+            lane < cand ? (direct ? float_key(__uint_as_float(sm.cand[lane])) : sm.small[lane]) : 0u;
         int gt = 0, eq = 0;
         for (int j = 0; j < cand; ++j) {
           const uint32_t x = __builtin_amdgcn_readlane(mykey, j);
@@ -368,7 +376,7 @@ __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_
       break;
     }
     const uint32_t range = hi - lo;
-    const int bits = 32 - __builtin_clz(range);
+    const int bits = range != 0u ? 32 - __builtin_clz(range) : 0;
     const int shift = bits > kDigitBits ? bits - kDigitBits : 0;
     uint32_t bin;
     int above, inbin;
@@ -376,8 +384,11 @@ __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_
         sm, need,
         [&](auto add) {
           for (int c = tid; c < nc; c += NT) {
-            const uint32_t x = sm.cand[c];
-            if (x >= lo && x <= hi) add((x - lo) >> shift);
+            const uint32_t x = float_key(__uint_as_float(sm.cand[c]));
+            if (x >= lo && (open || x <= hi)) {
+              const uint32_t d = (x - lo) >> shift; // < kBins unless open
+              add(d < (uint32_t)kBins ? d : (uint32_t)(kBins - 1));
+            }
           }
         },
         bin, above, inbin);
@@ -385,7 +396,11 @@ __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_
     cand = inbin;
     const uint32_t nlo = lo + (bin << shift);
     const uint32_t width = (1u << shift) - 1u;
-    hi = hi - nlo < width ? hi : nlo + width;
+    if (open) // a bin below the top is the whole interval; the top one is open
+      hi = bin == (uint32_t)(kBins - 1) ? 0xFFFFFFFFu : nlo + width;
+    else
+      hi = hi - nlo < width ? hi : nlo + width;
+    open = false;
     lo = nlo;
     if (inbin == need) { // the whole bin is taken
       thr = lo - 1u;
@@ -404,10 +419,72 @@ __device__ __forceinline__ void select_compacted(TopkShared &sm, int nc, uint32_
       sm,
       [&](int q) -> uint32_t {
         const int j = j0 + 64 * q;
-        return 64 * q < run && j < nc ? sm.cand[j] : 0u;
+        return 64 * q < run && j < nc ? float_key(__uint_as_float(sm.cand[j])) : 0u;
       },
       [&](int q) -> int32_t { return ib + (int32_t)sm.cidx[j0 + 64 * q]; }, thr, need_eq, all_ties,
       thr_ge, k, out);
+}
+
+// Whether a score's key is >= thr, from its raw bits b alone. Above +0's key
+// (POS) the passing scores are the positive ones with b >= thr - 2^31 (b read
+// as a signed integer: negative scores are negative). Below it they are every
+// score of sign 0 and the negative ones with ~b >= thr, i.e. b <= ~thr
+// unsigned, which every sign-0 b satisfies too (~thr >= 2^31), and so does -0
+// (0x80000000), as its key is +0's. Raw 0, the value of a slot past the row,
+// passes exactly when thr is below +0's key.
+template <bool POS> __device__ inline bool raw_at_least(uint32_t b, uint32_t thr) {
+  return POS ? (int32_t)b >= (int32_t)(thr & 0x7FFFFFFFu) : b <= ~thr;
+}
+
+// The exact count of the row's keys >= thr (over every wave's IPT raw scores
+// per lane, row index base + 64 i + lane; slots past the row hold 0) and,
+// when it lies in [k, kCandCap], the compaction of those scores' raw bits and
+// indices into LDS in index order, then the selection over them. Returns
+// whether the selection was made (else nothing is written and the caller runs
+// the full passes). Slots past the row that pass (only when thr is below +0's
+// key) have the highest indices, so they take the last positions and are
+// left out.
+template <int NT, int IPT, bool POS>
+__device__ __forceinline__ bool count_compact(TopkShared &sm, const uint32_t (&b)[IPT], uint32_t thr,
+                                              uint32_t smax, int E, int k, int base, int32_t ib,
+                                              int32_t *out) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t n0 = 0;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) n0 += (uint32_t)__popcll(__ballot(raw_at_least<POS>(b[i], thr)));
+  if (lane == 0) sm.red[wave] = n0;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += w < wave ? sm.red[w] : 0u;
+    total += sm.red[w];
+  }
+  if (!POS) total -= (uint32_t)(NT * IPT - E); // the slots past the row all pass
+  if (total < (uint32_t)k || total > (uint32_t)kCandCap) return false;
+  uint32_t at = before;
+  // the comparisons are made again rather than kept from the count: IPT
+  // ballots held across the barrier would not fit the scalar registers
+  uint32_t thr_c = thr;
+  asm volatile("" : "+s"(thr_c));
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const bool c = raw_at_least<POS>(b[i], thr_c);
+    const uint64_t mk = __ballot(c);
+    const uint32_t q = at + (uint32_t)lanes_below(mk);
+    if (c && (POS || q < total)) {
+      sm.cand[q] = b[i];
+      sm.cidx[q] = (uint32_t)(base + 64 * i + lane);
+    }
+    at += (uint32_t)__popcll(mk);
+  }
+  __syncthreads(); // the candidates are complete (and red is read)
+  // the sample's largest key bounds the first pass's bins, which need no
+  // per-score maximum: the row's keys above it share the top bin
+  select_compacted<NT>(sm, (int)total, thr, smax > thr ? smax : thr, k, ib, out);
+  return true;
 }
 
 // Selects the top k of a row of E > k scores, IPT keys per lane.
@@ -418,14 +495,16 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rounds = (E + NW * 64 - 1) / (NW * 64); // <= IPT
-  const int base = wave * rounds * 64;               // wave's first index
+  // Wave w holds row indices [w * IPT * 64, (w + 1) * IPT * 64): item i of a
+  // lane is index base + 64 i + lane, so every slot past the row is an index
+  // >= E, after every index of the row in item order.
+  const int base = wave * IPT * 64;
 
   // Loads through a buffer resource bounded by the row's E scores: past the
   // row they return 0 without a predicate and touch no memory; such items
-  // then get key 0 (every visible key is > 0x007FFFFF). The item step is part
-  // of the vector offset, which the hardware checks against the bound (the
-  // scalar offset is not checked).
+  // get key 0 when keys are formed (every visible key is > 0x007FFFFF). The
+  // item step is part of the vector offset, which the hardware checks against
+  // the bound (the scalar offset is not checked).
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(row), (short)0, E * 4, 0x00020000);
   // ---- the sample for the threshold estimate goes out first: 16 consecutive
@@ -439,7 +518,7 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
     const int q = tid + NT * u;
     sbits[u] = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)((q >> 4) * 256 + (q & 15)) * 4u, 0, 0);
   }
-  uint32_t key[IPT]; // the row's raw bits, keys once the estimate is made
+  uint32_t key[IPT]; // the row's raw bits; keys only on the full passes
   const uint32_t voff = (uint32_t)(base + lane) * 4u;
   const int left = E - base - lane; // item i is visible iff 64 * i < left
 #pragma unroll
@@ -462,7 +541,7 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
   // alone. Otherwise the estimate is dropped (nothing is decided by it) and
   // the full passes over the row follow.
   const bool sampled = E > kCandCap && 2 * k <= kCandCap;
-  uint32_t thr0 = 0u;
+  uint32_t thr0 = 0u, smax0 = 0u; // the estimate and the sample's largest key
   bool estimated = false;
   if (sampled) {
     uint32_t smp[SPT], smax = 0u, smin = 0xFFFFFFFFu, n_smp = 0u;
@@ -499,49 +578,26 @@ __device__ __forceinline__ void select_row(const float *row, int E, int k, int32
           },
           b0, a0, i0);
       thr0 = first_key_in_bin_near(smin - 1u, smax, b0, bin_edge_key(b0, h0, scale), vbin);
+      smax0 = smax;
       estimated = true;
     }
   }
-#pragma unroll
-  for (int i = 0; i < IPT; ++i)
-    key[i] = (i < rounds && 64 * i < left) ? float_key(__uint_as_float(key[i])) : 0u;
   if (estimated) {
-    uint32_t n0 = 0; // this wave's keys >= thr0 (key 0, past the row, is below thr0)
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) n0 += (uint32_t)__popcll(__ballot(key[i] >= thr0));
+    // Counted and compacted on the raw bits, one compare per score, with no
+    // key formed: per score this phase is bound by vector-ALU issue (16 waves
+    // x IPT scores per CU), and only the candidates are keyed, as they are
+    // read. A threshold at exactly +0's key moves to the key below it, which
+    // no score has (-0 keys as +0): the same scores pass, and the threshold
+    // then lies strictly above or below +0's key.
+    if (thr0 == 0x80000000u) thr0 = 0x7FFFFFFFu;
     // red was last read (block_max_min) before radix_pass's barriers
-    if (lane == 0) sm.red[wave] = n0;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      before += w < wave ? sm.red[w] : 0u;
-      total += sm.red[w];
-    }
-    if (total >= (uint32_t)k && total <= (uint32_t)kCandCap) {
-      uint32_t at = before, mx = 0u;
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        const bool c = key[i] >= thr0;
-        const uint64_t mk = __ballot(c);
-        if (c) {
-          const uint32_t q = at + (uint32_t)lanes_below(mk);
-          sm.cand[q] = key[i];
-          sm.cidx[q] = (uint32_t)(base + 64 * i + lane);
-        }
-        at += (uint32_t)__popcll(mk);
-        mx = key[i] > mx ? key[i] : mx; // the row's largest key is a candidate
-      }
-      mx = wave_max_u32(mx);
-      if (lane == 0) sm.red[16 + wave] = mx; // red[0, NW) is still being read
-      __syncthreads();
-      mx = 0u;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) mx = sm.red[16 + w] > mx ? sm.red[16 + w] : mx;
-      select_compacted<NT>(sm, (int)total, thr0, mx, k, ib, out);
+    if (thr0 > 0x80000000u ? count_compact<NT, IPT, true>(sm, key, thr0, smax0, E, k, base, ib, out)
+                           : count_compact<NT, IPT, false>(sm, key, thr0, smax0, E, k, base, ib, out))
       return;
-    }
   }
+  // keys for the full passes
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) key[i] = 64 * i < left ? float_key(__uint_as_float(key[i])) : 0u;
 
   // ---- the row's extremes, for the full passes
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, unused = 0u;

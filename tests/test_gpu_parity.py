@@ -261,16 +261,27 @@ def test_topk_wide_rows_every_threshold_path_exact(k):
     only some (runs of equal scores), too many keys above it (heavy ties, a
     crowded bin under far outliers) and too few (the sampled positions hold
     the largest scores) -- at several lengths; every row exact against the
-    oracle's top-k of the same fp32 values."""
+    oracle's top-k of the same fp32 values. Two more families place the
+    estimate below +0 (every score negative: the slots past a row's end then
+    pass it too and must be left out) and among runs of -0/+0 (most scores
+    signed zeros, a few positive), and the lengths leave the last wave of each
+    key bucket part-filled."""
     log("topk wide rows k %d" % k)
     W = 65536
     rng = np.random.default_rng(9000 + k)
     vals, E = [], []
-    for e in (4097, 20000, 32768, 65536):
+    for e in (4097, 20000, 32768, 40000, 65536):
         fams = _adversarial_rows(W, rng)
         boosted = rng.standard_normal(W).astype(np.float32)
         boosted[_sampled_positions(e)] += 100.0
         fams.append(boosted)
+        fams.append((-1.0 - np.abs(rng.standard_normal(W))).astype(np.float32))
+        zeros = np.where(rng.random(W) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        pos = rng.random(W) < 0.03
+        zeros[pos] = np.abs(rng.standard_normal(int(pos.sum()))).astype(np.float32) + 0.5
+        neg = rng.random(W) < 0.3
+        zeros[neg] = -np.abs(rng.standard_normal(int(neg.sum()))).astype(np.float32) - 0.5
+        fams.append(zeros)
         for row in fams:
             vals.append(row)
             E.append(e)
