@@ -208,18 +208,34 @@ __device__ inline int32_t wave_incl_scan(int32_t v) {
   return v;
 }
 
-// The range of work group c when no schedule buffer is given: the wave
-// computes what the schedule builder would write for entries c and c + 1
-// (same costs: ceil(len / BK) blocks per non-empty sequence plus the decode
-// entry cost; range c starts at unit floor(c * N / n_ctas) of the N units),
-// from all B <= kInlineSplitMaxSegs lengths at once, 64 sequences per lane
-// slot. With two work groups per SIMD (lead_ctas > 0) the shares are
-// weighted instead: the first lead_ctas groups, dispatched first and one per
-// SIMD, win issue arbitration over the second group on their SIMD and take
-// 4/3 of a share each (range c starts at floor(cum(c) * N / cum(n_ctas)),
-// cum(c) = 4 min(c, lead) + 3 max(c - lead, 0); MXFP4 decode 65.0 -> 63.7 us,
-// MTP 42.1 -> 41.1 us, over a four-copy pool rotation, two runs each).
-__device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
+// Whether ranges are dealt to the XCDs in contiguous eighths (see range_of).
+__device__ inline bool xcd_ranges(const LogitsArgs &a) {
+  const int n8 = a.n_ctas >> 3;
+  return (a.n_ctas & 7) == 0 && (a.lead_ctas == 0 || (n8 & 1) == 0);
+}
+
+// The range (schedule entry) that work group c takes. Work groups go to the
+// XCDs in turn (c runs on XCD c % 8), so group c takes range
+// (c % 8) * (n / 8) + c / 8: each XCD covers one contiguous eighth of the
+// work, and a sequence's query and block-table rows are fetched into one
+// XCD's L2 rather than all eight (batched decode 31.3 -> 30.9 us, same bits).
+__device__ inline int range_of(const LogitsArgs &a, int c) {
+  return xcd_ranges(a) ? (c & 7) * (a.n_ctas >> 3) + (c >> 3) : c;
+}
+
+// Range r when no schedule buffer is given: the wave computes what the
+// schedule builder would write for entries r and r + 1 (same costs:
+// ceil(len / BK) blocks per non-empty sequence plus the decode entry cost;
+// range r starts at unit floor(r * N / n_ctas) of the N units), from all
+// B <= kInlineSplitMaxSegs lengths at once, 64 sequences per lane slot. With
+// two work groups per SIMD (lead_ctas > 0) the shares are weighted instead:
+// the first lead_ctas groups, dispatched first and one per SIMD, win issue
+// arbitration over the second group on their SIMD and take 4/3 of a share
+// each (range r starts at floor(cum(r) * N / cum(n_ctas)); with ranges in
+// group order cum(r) = 4 min(r, lead) + 3 max(r - lead, 0); MXFP4 decode
+// 65.0 -> 63.7 us, MTP 42.1 -> 41.1 us, over a four-copy pool rotation, two
+// runs each).
+__device__ inline int32_t own_range(const LogitsArgs &a, int r, Walk &w) {
   constexpr int kChunks = kInlineSplitMaxSegs / 64;
   const int lane = threadIdx.x & 63;
   const int32_t entry = decode_entry_cost(a.next_n, a.block_tokens); // as the schedule builder
@@ -241,6 +257,8 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
     }
   }
   const int64_t N = total;
+  const bool xcd = xcd_ranges(a);
+  const int64_t n8 = a.n_ctas >> 3;
   int32_t len0 = 0; // length of the range's first sequence
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -249,9 +267,15 @@ __device__ inline int32_t own_range(const LogitsArgs &a, int c, Walk &w) {
     // denominator (<= 2^20) are exact, and a non-integer quotient (< 2^31)
     // lies at least 1/denominator from an integer, far beyond the division's
     // rounding error (< 2^-22), so truncation gives the floor
-    const int64_t ce = c + e;
+    const int64_t ce = r + e;
     int64_t num = ce, den = a.n_ctas;
-    if (a.lead_ctas > 0) {
+    if (a.lead_ctas > 0 && xcd) {
+      // lead_ctas = n / 2: the work groups c < n / 2 take the first half of
+      // every XCD's eighth of the ranges
+      const int64_t h = n8 >> 1, x = ce / n8, y = ce - x * n8;
+      num = 7 * h * x + 4 * (y < h ? y : h) + 3 * (y > h ? y - h : 0);
+      den = 7 * h * 8;
+    } else if (a.lead_ctas > 0) {
       const int64_t lead = a.lead_ctas;
       num = 4 * (ce < lead ? ce : lead) + 3 * (ce > lead ? ce - lead : 0);
       den = 4 * lead + 3 * (a.n_ctas - lead);
@@ -629,7 +653,7 @@ __global__ __launch_bounds__(64) void mqa_logits_kernel(LogitsArgs a) {
   static_assert(sizeof(ring) + sizeof(st) ==
                     decode_lds_bytes(DT == IDX_FP8_E4M3, TPB * kTile, NROW),
                 "the recommended work-group count assumes this LDS size");
-  const int c = blockIdx.x;
+  const int c = range_of(a, blockIdx.x);
   Walk w;
   int32_t len0;
   if (a.cta_info != nullptr) {

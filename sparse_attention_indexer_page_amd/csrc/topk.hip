@@ -147,6 +147,8 @@ struct TopkShared {
   uint32_t cidx[kCandCap]; // row index of cand[i] when the candidates are a sampled threshold's
   uint32_t small[kRankCap];
   uint32_t red[3 * 16];
+  uint32_t ered[2 * 16]; // the output's per-wave counts (their own, so no
+                         // barrier has to separate them from reads of red)
   uint32_t sel[3]; // bin, count above it, count in it
   uint32_t ncand;
   uint32_t nsmall;
@@ -260,17 +262,16 @@ __device__ __forceinline__ void emit_selection(TopkShared &sm, KeyAt key_at, Idx
       n_eq += __popcll(__ballot(x == thr));
     }
   }
-  __syncthreads(); // every thread is done reading red and sel
   if (lane == 0) {
-    sm.red[wave] = n_gt;
-    sm.red[16 + wave] = n_eq;
+    sm.ered[wave] = n_gt;
+    sm.ered[16 + wave] = n_eq;
   }
   __syncthreads();
   int gt_before = 0, eq_before = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    gt_before += w < wave ? (int)sm.red[w] : 0;
-    eq_before += w < wave ? (int)sm.red[16 + w] : 0;
+    gt_before += w < wave ? (int)sm.ered[w] : 0;
+    eq_before += w < wave ? (int)sm.ered[16 + w] : 0;
   }
 
   // ---- writing pass in index order (the comparisons are made again rather
